@@ -1,0 +1,228 @@
+// libsia C ABI: host-side validation, workspace layout and dispatch.
+// Every check happens before the first launch; kernels run asynchronously on
+// the caller's stream and the library never synchronizes or allocates.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "sia_internal.hpp"
+
+namespace sia {
+
+static thread_local std::string g_last_hip_error;
+
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+static int hip_fail(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return SIA_ERR_HIP;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int check_seq(const sia_seqmap* s) {
+  if (!s) return SIA_ERR_INVALID_ARG;
+  if (s->num_tokens < 0) return SIA_ERR_INVALID_ARG;
+  if (s->num_tokens == 0) return SIA_OK;
+  if (!s->q_seq || !s->q_pos || !s->block_table) return SIA_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->max_pages < 1 || s->num_pages < 1 || s->max_visible < 1) return SIA_ERR_INVALID_ARG;
+  if (s->page_size != 64) return SIA_ERR_UNSUPPORTED;
+  if ((int64_t)s->max_visible > (int64_t)s->max_pages * s->page_size) return SIA_ERR_INVALID_ARG;
+  if ((int64_t)s->num_pages * s->page_size > INT32_MAX) return SIA_ERR_UNSUPPORTED;
+  return SIA_OK;
+}
+
+static int check_indexer(const sia_indexer_in* in) {
+  if (!in || !in->q || !in->w || !in->k_pool) return SIA_ERR_INVALID_ARG;
+  if (in->heads < 1 || in->dim < 1) return SIA_ERR_INVALID_ARG;
+  if (in->dtype == SIA_F32) {
+    if (in->heads > 64 || (int64_t)in->heads * in->dim > 4096) return SIA_ERR_UNSUPPORTED;
+  } else if (in->dtype == SIA_FP8_E4M3) {
+    if (!in->q_scale || !in->k_scale) return SIA_ERR_INVALID_ARG;
+    if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
+    if (!aligned16(in->q) || !aligned16(in->k_pool)) return SIA_ERR_INVALID_ARG;
+  } else {
+    return SIA_ERR_UNSUPPORTED;
+  }
+  return SIA_OK;
+}
+
+static int check_scores(const float* scores, int64_t ld, const sia_seqmap* s) {
+  if (!scores || !aligned16(scores)) return SIA_ERR_INVALID_ARG;
+  if (ld < 1 || (ld & 3) != 0) return SIA_ERR_INVALID_ARG;
+  if (s->num_tokens > 0 && ld < s->max_visible) return SIA_ERR_INVALID_ARG;
+  return SIA_OK;
+}
+
+static int check_kv(const sia_kv_in* kv, sia_dtype q_dtype, int heads, int K) {
+  if (!kv || !kv->kv_pool) return SIA_ERR_INVALID_ARG;
+  if (K < 1) return SIA_ERR_INVALID_ARG;
+  if (kv->latent_dim < 1 || kv->rope_dim < 0) return SIA_ERR_INVALID_ARG;
+  if (kv->dtype == SIA_F32) {
+    if (q_dtype != SIA_F32) return SIA_ERR_UNSUPPORTED;
+    if (heads < 1 || heads > 64 || kv->latent_dim + kv->rope_dim > 1024 || K > 2048) return SIA_ERR_UNSUPPORTED;
+    return SIA_OK;
+  }
+  if (kv->dtype != SIA_BF16 && kv->dtype != SIA_FP8_E4M3) return SIA_ERR_UNSUPPORTED;
+  if (q_dtype != SIA_BF16) return SIA_ERR_UNSUPPORTED;
+  if (kv->latent_dim != 512 || kv->rope_dim != 64) return SIA_ERR_UNSUPPORTED;
+  if (heads != 32 && heads != 64 && heads != 128) return SIA_ERR_UNSUPPORTED;
+  if (!aligned16(kv->kv_pool)) return SIA_ERR_INVALID_ARG;
+  if (kv->dtype == SIA_FP8_E4M3) {
+    if (!kv->kv_scale) return SIA_ERR_INVALID_ARG;
+    const bool page_tile = kv->scale_tokens == 64 && kv->scale_elems == 512;
+    const bool tok_tile = kv->scale_tokens == 1 && kv->scale_elems == 128;
+    if (!page_tile && !tok_tile) return SIA_ERR_UNSUPPORTED;
+  }
+  return SIA_OK;
+}
+
+static int mla_common(const void* q, sia_dtype q_dtype, int heads, const sia_kv_in* kv, const sia_seqmap* seq,
+                      const int32_t* idx, int K, float scale, void* out) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_kv(kv, q_dtype, heads, K);
+  if (rc) return rc;
+  if (seq->num_tokens == 0) return SIA_OK;
+  if (!q || !idx || !out) return SIA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return SIA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale != scale) return SIA_ERR_INVALID_ARG;
+  return SIA_OK;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static int64_t fused_ld(const sia_seqmap* s) { return ((int64_t)s->max_visible + 63) / 64 * 64; }
+
+}  // namespace sia
+
+using namespace sia;
+
+extern "C" {
+
+const char* sia_status_string(int status) {
+  switch (status) {
+    case SIA_OK: return "ok";
+    case SIA_ERR_INVALID_ARG: return "invalid argument";
+    case SIA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SIA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SIA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* sia_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* scores, int64_t ld,
+                     hipStream_t stream) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_indexer(in);
+  if (rc) return rc;
+  rc = check_scores(scores, ld, seq);
+  if (rc) return rc;
+  const hipError_t e = launch_index_scores(*in, seq_args(*seq), scores, ld, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, int32_t order, int32_t* idx,
+             float* vals, hipStream_t stream) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_scores(scores, ld, seq);
+  if (rc) return rc;
+  if (K < 1 || K > 2048 || (order != 0 && order != 1) || !idx) return K > 2048 ? SIA_ERR_UNSUPPORTED : SIA_ERR_INVALID_ARG;
+  const hipError_t e = launch_topk(scores, ld, seq_args(*seq), K, order, idx, vals, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+static int mla_entry(bool decode, const void* q, sia_dtype q_dtype, int32_t heads, const sia_kv_in* kv,
+                     const sia_seqmap* seq, const int32_t* idx, int32_t K, float softmax_scale, void* out,
+                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = mla_common(q, q_dtype, heads, kv, seq, idx, K, softmax_scale, out);
+  if (rc) return rc;
+  if (seq->num_tokens == 0) return SIA_OK;
+  int splits = 1;
+  if (decode && kv->dtype != SIA_F32) {
+    splits = mla_splits(seq->num_tokens, K, heads);
+    const size_t need = mla_workspace_bytes(seq->num_tokens, K, heads, kv->latent_dim);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return SIA_ERR_WORKSPACE;
+  }
+  const hipError_t e =
+      launch_sparse_mla(q, heads, *kv, seq_args(*seq), idx, K, softmax_scale, out, lse, splits, ws, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+int sia_sparse_mla_decode(const void* q, sia_dtype q_dtype, int32_t heads, const sia_kv_in* kv,
+                          const sia_seqmap* seq, const int32_t* idx, int32_t K, float softmax_scale, void* out,
+                          float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return mla_entry(true, q, q_dtype, heads, kv, seq, idx, K, softmax_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int sia_sparse_mla_prefill(const void* q, sia_dtype q_dtype, int32_t heads, const sia_kv_in* kv,
+                           const sia_seqmap* seq, const int32_t* idx, int32_t K, float softmax_scale, void* out,
+                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return mla_entry(false, q, q_dtype, heads, kv, seq, idx, K, softmax_scale, out, lse, ws, ws_bytes, stream);
+}
+
+size_t sia_workspace_size(int32_t op, const sia_seqmap* seq, int32_t K, int32_t heads, int32_t latent_dim) {
+  if (check_seq(seq) != SIA_OK || K < 1 || heads < 1 || latent_dim < 1) return (size_t)-1;
+  const int T = seq->num_tokens;
+  switch (op) {
+    case SIA_OP_TOPK:
+    case SIA_OP_MLA_PREFILL:
+      return 0;
+    case SIA_OP_MLA_DECODE:
+      return mla_workspace_bytes(T, K, heads, latent_dim);
+    case SIA_OP_INDEX_SELECT_ATTEND: {
+      if (T == 0) return 0;
+      const size_t scores = align256((size_t)T * fused_ld(seq) * sizeof(float));
+      const size_t ids = align256((size_t)T * K * sizeof(int32_t));
+      return scores + ids + align256(mla_workspace_bytes(T, K, heads, latent_dim));
+    }
+    default:
+      return (size_t)-1;
+  }
+}
+
+int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dtype q_dtype, int32_t heads,
+                            const sia_kv_in* kv, const sia_seqmap* seq, int32_t K, int32_t order,
+                            float softmax_scale, int32_t* idx_out, void* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_indexer(in);
+  if (rc) return rc;
+  if (K < 1 || (order != 0 && order != 1)) return SIA_ERR_INVALID_ARG;
+  if (K > 2048) return SIA_ERR_UNSUPPORTED;
+  rc = mla_common(q_mla, q_dtype, heads, kv, seq, idx_out ? idx_out : (const int32_t*)ws, K, softmax_scale, out);
+  if (rc) return rc;
+  if (seq->num_tokens == 0) return SIA_OK;
+  const size_t need = sia_workspace_size(SIA_OP_INDEX_SELECT_ATTEND, seq, K, heads, kv->latent_dim);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
+  const int T = seq->num_tokens;
+  const int64_t ld = fused_ld(seq);
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* scores = reinterpret_cast<float*>(base);
+  base += align256((size_t)T * ld * sizeof(float));
+  int32_t* ids = idx_out ? idx_out : reinterpret_cast<int32_t*>(base);
+  base += align256((size_t)T * K * sizeof(int32_t));
+  void* mla_ws = base;
+
+  const SeqArgs s = seq_args(*seq);
+  hipError_t e = launch_index_scores(*in, s, scores, ld, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_topk(scores, ld, s, K, order, ids, nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  const int splits = kv->dtype == SIA_F32 ? 1 : mla_splits(T, K, heads);
+  e = launch_sparse_mla(q_mla, heads, *kv, s, ids, K, softmax_scale, out, lse, splits, mla_ws, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+}  // extern "C"

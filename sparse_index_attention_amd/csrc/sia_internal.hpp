@@ -1,0 +1,41 @@
+// Host-side declarations shared between the C ABI layer and the kernel sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sia.h"
+
+namespace sia {
+
+// Plain copy of the sequence map handed to every kernel.
+struct SeqArgs {
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+  int32_t T;
+  int32_t batch;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t max_visible;
+};
+
+inline SeqArgs seq_args(const sia_seqmap& s) {
+  return SeqArgs{s.q_seq, s.q_pos, s.block_table, s.num_tokens, s.batch, s.max_pages, s.num_pages, s.max_visible};
+}
+
+int num_cus();
+
+// indexer.hip
+hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,
+                               hipStream_t st);
+// topk.hip
+hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
+                       float* vals, hipStream_t st);
+// sparse_mla.hip
+int mla_splits(int T, int K, int heads);
+size_t mla_workspace_bytes(int T, int K, int heads, int latent);
+hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, const SeqArgs& s,
+                             const int32_t* idx, int K, float scale, void* out, float* lse, int splits,
+                             void* ws, hipStream_t st);
+
+}  // namespace sia

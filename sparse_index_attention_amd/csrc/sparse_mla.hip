@@ -1,0 +1,518 @@
+// Step 3 — sparse MLA attention over the Top-K rows of a paged latent cache.
+//
+// [P1] "Day 0 Inference Adaptation and Optimization for Hybrid Attention Models",
+//      section "Sparse Attention Pipeline Optimization": the sparse kernel reads
+//      only the selected KV entries and runs block-wise fused attention on them.
+// [P3] "Day-One Inference Adaptation for Very Large Hybrid-Attention Models",
+//      section 3.2: tile by query block, aggregate over the selected positions,
+//      stage tiles in on-chip shared memory.
+// [P5] "Inference Adaptation and Performance Optimization for a Domestically
+//      Developed LLM's New Architecture", section 4 table: FP8 KV cache with
+//      per-token 128-element tiles (the per-page tile is also supported).
+//
+// MFMA path (bf16 / fp8 cache, latent 512 + rope 64): one workgroup = one query
+// token (all heads) x a contiguous share of its selected rows.  Wave w owns heads
+// [32w, 32w+32).  Per 32-row tile:
+//   * rows are gathered from the paged cache straight into LDS (16-byte direct
+//     global->LDS loads for bf16; fp8 rows go through registers and are
+//     dequantized to bf16 on the way), double buffered;
+//   * S^T[row, head] = KV_tile . Q^T on v_mfma_f32_32x32x16_bf16: the KV tile is
+//     the LDS operand, the wave's 32 query heads stay in registers for the
+//     whole token;
+//   * online softmax per head is lane-local (each lane owns one head column);
+//   * O^T[vcol, head] += V^T . P^T: P^T comes straight from the S^T accumulator
+//     (the row order inside the MFMA K dimension is chosen to match it) and V^T
+//     is read with ds_read_b64_tr_b16 transposing loads.
+// The LDS tile is row-major (72 16-byte chunks per row) with the chunk index
+// XOR-swizzled by f(row) = 2*(row%4) + (row/4)%2, which keeps both the 128-bit
+// row reads and the transposing reads free of bank conflicts.
+//
+// Decode splits a token's rows over several workgroups; each writes a partial
+// (O normalised over its rows, LSE) and a combine kernel merges them with
+// softmax weights exp(lse_s - LSE) in a fixed order.
+#include "sia_common.hpp"
+#include "sia_internal.hpp"
+
+namespace sia {
+
+struct MlaArgs {
+  const void* q;
+  const void* kv;
+  const float* kv_scale;
+  int scale_tokens, scale_elems;  // fp8 tiles
+  int H;
+  int Dc, Dr;
+  SeqArgs s;
+  const int32_t* idx;
+  int K;
+  float scale_log2;  // softmax_scale * log2(e)
+  int splits;
+  int rows_per_split;
+  void* out;    // final output (splits == 1)
+  float* lse;   // nullable
+  float* ws_o;  // [T, splits, H, Dc] partial outputs (splits > 1)
+  float* ws_lse;
+};
+
+// ---------------------------------------------------------------------------
+// float32 path (small dims): one workgroup per (token, head).
+// ---------------------------------------------------------------------------
+constexpr int kF32MaxDim = 1024;
+constexpr int kF32MaxK = 2048;
+
+__global__ __launch_bounds__(256) void k_sparse_mla_f32(MlaArgs a) {
+  __shared__ float sq[kF32MaxDim];
+  __shared__ float sl[kF32MaxK];
+  __shared__ int64_t sslot[kF32MaxK];
+  __shared__ float red[8];
+  const int t = blockIdx.x, h = blockIdx.y;
+  const int D = a.Dc + a.Dr, tid = threadIdx.x;
+  const int b = clampi(a.s.q_seq[t], 0, a.s.batch - 1);
+  const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
+  const float* q = (const float*)a.q + ((int64_t)t * a.H + h) * D;
+  const float* kv = (const float*)a.kv;
+  for (int i = tid; i < D; i += blockDim.x) sq[i] = q[i];
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int j = tid; j < a.K; j += blockDim.x) {
+    const int p = a.idx[(int64_t)t * a.K + j];
+    float l = -INFINITY;
+    int64_t slot = -1;
+    if (p >= 0 && p < a.s.max_visible) {
+      slot = page_slot(table, p, a.s.num_pages);
+      const float* r = kv + slot * D;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(sq[d], r[d], dot);
+      l = dot * a.scale_log2;
+    }
+    sl[j] = l;
+    sslot[j] = slot;
+    mx = fmaxf(mx, l);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) mx = fmaxf(mx, red[i]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = tid; j < a.K; j += blockDim.x) {
+    const float p = sslot[j] >= 0 ? exp2f(sl[j] - mx) : 0.f;
+    sl[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if ((tid & 63) == 0) red[tid >> 6] = sum;
+  __syncthreads();
+  sum = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) sum += red[i];
+  float* out = (float*)a.out + ((int64_t)t * a.H + h) * a.Dc;
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  for (int d = tid; d < a.Dc; d += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < a.K; ++j)
+      if (sslot[j] >= 0) acc = fmaf(sl[j], kv[sslot[j] * D + d], acc);
+    out[d] = acc * inv;
+  }
+  if (tid == 0 && a.lse)
+    a.lse[(int64_t)t * a.H + h] = sum > 0.f ? (mx + log2f(sum)) * 0.6931471805599453f : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path.
+// ---------------------------------------------------------------------------
+constexpr int kDc = 512, kDr = 64, kD = kDc + kDr;
+constexpr int kChunks = kD / 8;                   // 72 chunks of 8 bf16 (16 bytes) per row
+constexpr int kRowsTile = 32;
+constexpr int kTileBytes = kRowsTile * kD * 2;   // 36864
+
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+__device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+typedef __attribute__((address_space(3))) v8bf lds_v8bf;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
+__device__ __forceinline__ v4bf lds_tr16(lds_u8* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(base + byte_off));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_hw(lo) | ((uint32_t)f32_to_bf16_hw(hi) << 16);
+}
+
+// LDS tile layout: 72 chunks of 16 bytes per row, grouped 8 chunks at a time:
+//   slot(row, c) = (c / 8) * 256 + row * 8 + ((c % 8) ^ swz(row)),  byte = 16 * slot.
+// A wave's 16-byte direct load then fills 64 consecutive slots (8 rows x one
+// 128-byte chunk group), and every LDS read is one per-lane base register plus a
+// compile-time immediate.
+//
+// The first QREG K-steps of the query operand stay in registers; the rest is
+// parked in LDS (per wave, one 16-byte slot per lane and step) to leave room for
+// the 256-register output accumulator.
+template <bool FP8> struct MlaCfg { static constexpr int QREG = FP8 ? 16 : 18; };
+
+template <int NW, bool FP8>
+__global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int QREG = MlaCfg<FP8>::QREG, QLDS = 36 - QREG;
+  constexpr int TPR = NT / kRowsTile;          // threads per row in the fp8 gather
+  constexpr int kFp8Loads = 40 / TPR;          // 640-byte rows = 40 loads of 16 bytes
+  __shared__ __attribute__((aligned(16))) unsigned char tile[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char qlds[NW * QLDS * 64 * 16];
+  __shared__ int32_t sslot[3][kRowsTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, nn = lane & 31;
+  lds_u8* const tl = (lds_u8*)tile;
+  lds_u8* const ql = (lds_u8*)qlds + wave * (QLDS * 64 * 16) + lane * 16;
+  const int split = blockIdx.x % a.splits;
+  const int t = blockIdx.x / a.splits;
+  const int j0 = split * a.rows_per_split;
+  int j1 = j0 + a.rows_per_split;
+  j1 = j1 < a.K ? j1 : a.K;
+  const int nrows = j1 > j0 ? j1 - j0 : 0;
+  const int ntiles = (nrows + kRowsTile - 1) / kRowsTile;
+  const int b = clampi(a.s.q_seq[t], 0, a.s.batch - 1);
+  const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
+  const int32_t* irow = a.idx + (int64_t)t * a.K;
+  const int head = wave * 32 + nn;
+  const unsigned char* kvb = (const unsigned char*)a.kv;
+
+  // slot numbers of tile i's rows (-1: no row)
+  auto fill_slots = [&](int i) {
+    if (tid < kRowsTile) {
+      const int j = j0 + i * kRowsTile + tid;
+      int slot = -1;
+      if (j < j1) {
+        const int p = irow[j];
+        if (p >= 0 && p < a.s.max_visible) slot = (int)page_slot(table, p, a.s.num_pages);
+      }
+      sslot[i % 3][tid] = slot;
+    }
+  };
+
+  // ---- gather: bf16 rows go global -> LDS directly --------------------------
+  // wave instruction (row group rg, chunk group m) covers rows 8rg..8rg+7 and
+  // chunks 8m..8m+7; lane L: row 8rg + L/8, chunk 8m + ((L%8) ^ swz(row)).
+  const int g_sub = lane & 7;
+  auto issue_bf16 = [&](int i) {
+    const int32_t* ss = sslot[i % 3];
+    lds_u8* dst = tl + (i & 1) * kTileBytes;
+#pragma unroll
+    for (int rg = wave; rg < 4; rg += NW) {
+      const int r = 8 * rg + (lane >> 3);
+      const int slot = ss[r] >= 0 ? ss[r] : 0;
+      const unsigned char* src = kvb + (int64_t)slot * (kD * 2) + 16 * (g_sub ^ swz(r));
+#pragma unroll
+      for (int m = 0; m < 9; ++m)
+        __builtin_amdgcn_global_load_lds(src + 128 * m, (lds_void*)(dst + (m * 256 + 64 * rg) * 16), 16, 0, 0);
+    }
+  };
+
+  // ---- gather: fp8 rows go through registers and are dequantized to bf16 ----
+  // thread -> row tid / TPR, 16-byte source chunks c = tid % TPR + TPR * m
+  v4i stage[FP8 ? kFp8Loads : 1];
+  float stage_scale[FP8 ? kFp8Loads : 1];
+  const int f_row = tid / TPR, f_sub = tid % TPR;
+  auto issue_fp8 = [&](int i) {
+    const int32_t* ss = sslot[i % 3];
+    const int slot = ss[f_row] >= 0 ? ss[f_row] : 0;
+    const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
+    const int page = slot >> 6, tok = slot & 63;
+    const int tiles_tok = kPage / a.scale_tokens, tiles_el = kDc / a.scale_elems;
+    const int64_t sbase = ((int64_t)page * tiles_tok + tok / a.scale_tokens) * tiles_el;
+#pragma unroll
+    for (int m = 0; m < kFp8Loads; ++m) {
+      const int c = f_sub + TPR * m;
+      stage[m] = *(const v4i*)(src + 16 * TPR * m);
+      stage_scale[m] = c < 32 ? a.kv_scale[sbase + (16 * c) / a.scale_elems] : 1.f;
+    }
+  };
+  auto commit_fp8 = [&](int i) {
+    lds_u8* dst = tl + (i & 1) * kTileBytes;
+    const int r = f_row, sw = swz(r);
+#pragma unroll
+    for (int m = 0; m < kFp8Loads; ++m) {
+      const int c = f_sub + TPR * m;
+      const v4i v = stage[m];
+      if (c < 32) {
+        const float sc = stage_scale[m];
+        uint32_t o[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float2 f0 = fp8x2_to_f32<false>((uint32_t)v[w]);
+          const float2 f1 = fp8x2_to_f32<true>((uint32_t)v[w]);
+          o[2 * w] = pack_bf16x2(f0.x * sc, f0.y * sc);
+          o[2 * w + 1] = pack_bf16x2(f1.x * sc, f1.y * sc);
+        }
+        const int c0 = 2 * c, c1 = 2 * c + 1;
+        *(lds_v4i*)(dst + ((c0 >> 3) * 256 + r * 8 + ((c0 & 7) ^ sw)) * 16) =
+            v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        *(lds_v4i*)(dst + ((c1 >> 3) * 256 + r * 8 + ((c1 & 7) ^ sw)) * 16) =
+            v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      } else {
+        const int cr = 64 + (c - 32);
+        *(lds_v4i*)(dst + ((cr >> 3) * 256 + r * 8 + ((cr & 7) ^ sw)) * 16) = v;
+      }
+    }
+  };
+
+  // ---- query operand: Q^T[depth, head], lane (hh, nn): head nn, chunk 2i + hh
+  v8bf qb[QREG];
+  {
+    const v8bf* qr = (const v8bf*)((const uint16_t*)a.q + ((int64_t)t * a.H + head) * kD);
+#pragma unroll
+    for (int i = 0; i < QREG; ++i) qb[i] = qr[2 * i + hh];
+#pragma unroll
+    for (int i = QREG; i < 36; ++i) *(lds_v8bf*)(ql + (i - QREG) * 1024) = qr[2 * i + hh];
+  }
+
+  // per-lane LDS read bases (see the layout note above)
+  //  S^T A operand, step st = 4k + mm: chunk 2st + hh -> group k, in-group 2mm + hh
+  int sbase[4];
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) sbase[mm] = 16 * (nn * 8 + ((2 * mm + hh) ^ swz(nn)));
+  //  V^T A operand via transposing reads: source lane s' = lane%16 gives row
+  //  offset jrow = s'/4 and vcol quad qd = s'%4; lane group g = lane/16.
+  const int g = lane >> 4, sp = lane & 15, jrow = sp >> 2, qd = sp & 3;
+  const int vrow0 = 4 * (g >> 1) + jrow;            // + 8a + 16mf
+  const int vsw = swz(vrow0);                       // same for every a, mf
+  int vbase[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    vbase[par] = 128 * vrow0 + 16 * ((4 * par + 2 * (g & 1) + (qd >> 1)) ^ vsw) + 8 * (qd & 1);
+
+  v16f o[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) o[v] = v16f{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (ntiles > 0) {
+    fill_slots(0);
+    __syncthreads();
+    if constexpr (FP8) {
+      issue_fp8(0);
+      commit_fp8(0);
+    } else {
+      issue_bf16(0);
+    }
+    if (ntiles > 1) fill_slots(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  for (int i = 0; i < ntiles; ++i) {
+    if (i + 1 < ntiles) {
+      if constexpr (FP8) issue_fp8(i + 1);
+      else issue_bf16(i + 1);
+    }
+    lds_u8* cur = tl + (i & 1) * kTileBytes;
+    const int32_t* ss = sslot[i % 3];
+
+    // S^T = KV . Q^T  (rows x heads)
+    v16f sacc = {};
+#pragma unroll
+    for (int st = 0; st < 36; ++st) {
+      const v8bf kf = *(lds_v8bf*)(cur + sbase[st & 3] + 4096 * (st >> 2));
+      const v8bf qf = st < QREG ? qb[st < QREG ? st : 0] : *(lds_v8bf*)(ql + (st - QREG) * 1024);
+      sacc = mfma_bf16(kf, qf, sacc);
+    }
+    // online softmax over the tile's rows (log2 domain); lane owns head nn,
+    // rows 8*(r/4) + 4*hh + r%4
+    float sv[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+      sv[r] = ss[row] >= 0 ? sacc[r] * a.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // lazy rescale: move the running max only when it grows by more than 2^8
+    const bool grow = tmax > m_run + 8.f;
+    if (__ballot(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[v][r] *= alpha;
+    }
+    float psum = 0.f;
+    v8bf pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = (m_run == -INFINITY) ? 0.f : fast_exp2(sv[r] - m_run);
+      psum += pv;
+      pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
+    }
+    l_run += psum;
+
+    // O^T += V^T . P^T ; MFMA mf covers tile rows 16mf + R(hh, jj)
+#pragma unroll
+    for (int vt = 0; vt < 16; ++vt) {
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf) {
+        const int imm = 4096 * (vt >> 1) + 2048 * mf;
+        const v4bf x0 = lds_tr16(cur, vbase[vt & 1] + imm);
+        const v4bf x1 = lds_tr16(cur, vbase[vt & 1] + imm + 1024);
+        const v8bf af = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[vt] = mfma_bf16(af, pb[mf], o[vt]);
+      }
+    }
+
+    if (i + 2 < ntiles) fill_slots(i + 2);
+    if constexpr (FP8) {
+      // the other buffer was last read in iteration i-1, before the previous barrier
+      if (i + 1 < ntiles) commit_fp8(i + 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- finish: normalise and write
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  if (a.splits == 1) {
+    uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + head) * kDc;
+#pragma unroll
+    for (int vt = 0; vt < 16; ++vt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int vc = 32 * vt + 8 * q4 + 4 * hh;
+        uint2 w;
+        w.x = pack_bf16x2(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv);
+        *(uint2*)(out + vc) = w;
+      }
+    if (a.lse && hh == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
+  } else {
+    const int64_t pidx = ((int64_t)t * a.splits + split) * a.H + head;
+    float* po = a.ws_o + pidx * kDc;
+#pragma unroll
+    for (int vt = 0; vt < 16; ++vt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int vc = 32 * vt + 8 * q4 + 4 * hh;
+        *(float4*)(po + vc) = make_float4(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv, o[vt][4 * q4 + 2] * inv,
+                                          o[vt][4 * q4 + 3] * inv);
+      }
+    if (hh == 0) a.ws_lse[pidx] = lse_v;
+  }
+}
+
+// Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, in split order.
+template <bool F32OUT>
+__global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= a.H) return;
+  const int S = a.splits, Dc = a.Dc;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, a.ws_lse[((int64_t)t * S + sp) * a.H + h]);
+  float tot = 0.f;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int sp = 0; sp < S; ++sp) {
+    const int64_t pidx = ((int64_t)t * S + sp) * a.H + h;
+    const float ls = a.ws_lse[pidx];
+    const float wgt = (mx == -INFINITY) ? 0.f : __expf(ls - mx);
+    tot += wgt;
+    if (wgt != 0.f) {
+      const float* po = a.ws_o + pidx * Dc;
+      for (int d = lane * 8, k = 0; k < 8; ++k) acc[k] = fmaf(wgt, po[d + k], acc[k]);
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  if (F32OUT) {
+    float* out = (float*)a.out + ((int64_t)t * a.H + h) * Dc + lane * 8;
+    for (int k = 0; k < 8; ++k) out[k] = acc[k] * inv;
+  } else {
+    uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + h) * Dc + lane * 8;
+    uint4 w;
+    w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    *(uint4*)out = w;
+  }
+  if (a.lse && lane == 0) a.lse[(int64_t)t * a.H + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
+}
+
+int mla_splits(int T, int K, int heads) {
+  if (T <= 0) return 1;
+  const int cus = num_cus();
+  int s = (cus + T - 1) / T;             // about one workgroup per CU
+  const int max_s = (K + kRowsTile * 2 - 1) / (kRowsTile * 2);  // keep >= 2 tiles per split
+  s = s > max_s ? max_s : s;
+  s = s > 32 ? 32 : s;
+  return s < 1 ? 1 : s;
+}
+
+size_t mla_workspace_bytes(int T, int K, int heads, int latent) {
+  const int s = mla_splits(T, K, heads);
+  if (s <= 1) return 0;
+  return (size_t)T * s * heads * ((size_t)latent + 1) * sizeof(float) + 256;
+}
+
+hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, const SeqArgs& s, const int32_t* idx,
+                             int K, float scale, void* out, float* lse, int splits, void* ws, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  MlaArgs a{};
+  a.q = q;
+  a.kv = kv.kv_pool;
+  a.kv_scale = kv.kv_scale;
+  a.scale_tokens = kv.scale_tokens;
+  a.scale_elems = kv.scale_elems;
+  a.H = heads;
+  a.Dc = kv.latent_dim;
+  a.Dr = kv.rope_dim;
+  a.s = s;
+  a.idx = idx;
+  a.K = K;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  if (kv.dtype == SIA_F32) {
+    a.splits = 1;
+    hipLaunchKernelGGL(k_sparse_mla_f32, dim3(s.T, heads), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  a.splits = splits < 1 ? 1 : splits;
+  int rps = (K + a.splits - 1) / a.splits;
+  rps = (rps + kRowsTile - 1) / kRowsTile * kRowsTile;
+  a.rows_per_split = rps;
+  if (a.splits > 1) {
+    a.ws_o = (float*)ws;
+    a.ws_lse = a.ws_o + (size_t)s.T * a.splits * heads * kDc;
+  }
+  const dim3 grid((unsigned)((int64_t)s.T * a.splits));
+  const bool fp8 = kv.dtype == SIA_FP8_E4M3;
+#define SIA_LAUNCH_MLA(NW)                                                                   \
+  if (fp8)                                                                                   \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true>), grid, dim3(NW * 64), 0, st, a);        \
+  else                                                                                       \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false>), grid, dim3(NW * 64), 0, st, a);
+  if (heads == 128) {
+    SIA_LAUNCH_MLA(4)
+  } else if (heads == 64) {
+    SIA_LAUNCH_MLA(2)
+  } else {
+    SIA_LAUNCH_MLA(1)
+  }
+#undef SIA_LAUNCH_MLA
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL(k_mla_combine<false>, dim3(s.T, (heads + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sia

@@ -1,0 +1,116 @@
+"""Helpers shared by the GPU parity tests: upload a workload, run the oracle on
+the same inputs, and compare with the stated tolerances."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+import oracle as O
+from sparse_index_attention_amd import sia
+from sparse_index_attention_amd import workloads as W
+
+# Score tolerance: |g - o| <= 1e-3 |o| + eps * A, with A the same score computed
+# on absolute values (sum_h |w_h| qs ks sum_d |q_hd k_sd|), i.e. the magnitude
+# that bounds any summation-order or accumulator-rounding error.  eps is 2^-11
+# for the fp8 MFMA path (its internal accumulation rounds at ~2^-14 of A) and
+# 2^-16 for the fp32 path.
+SCORE_REL = 1e-3
+SCORE_EPS = {"fp8": 2.0 ** -11, "f32": 2.0 ** -16}
+# Attention tolerance: |g - o| <= ATOL + RTOL |o| elementwise.
+ATT_TOL = {"bf16": (2e-2, 1e-2), "fp8": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
+LSE_ATOL = {"bf16": 2e-2, "fp8": 2e-2, "f32": 1e-4}
+
+
+def dev(x: np.ndarray, device="cuda"):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+@functools.lru_cache(maxsize=8)
+def workload(name):
+    return W.make_workload(name)
+
+
+def upload(wl: W.Workload, device="cuda"):
+    c = wl.cfg
+    seq = sia.SeqMap(dev(wl.q_seq), dev(wl.q_pos), dev(wl.block_table), wl.num_pages, wl.max_visible)
+    if c["idx_dtype"] == "f32":
+        ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik))
+    else:
+        ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik), dev(wl.iq_scale), dev(wl.ik_scale))
+    if c["kv_dtype"] == "fp8":
+        st, se = c["kv_scale"]
+        kv = sia.LatentKV(dev(wl.kv), c["Dc"], c["Dr"], dev(wl.kv_scale), st, se)
+    else:
+        kv = sia.LatentKV(dev(wl.kv), c["Dc"], c["Dr"])
+    return seq, ix, dev(wl.q), kv
+
+
+def score_bound_row(wl: W.Workload, t: int) -> np.ndarray:
+    """A[t, s] for s <= q_pos[t] (see SCORE_EPS)."""
+    idx = wl.oracle_indexer()
+    b, pos = int(wl.q_seq[t]), int(wl.q_pos[t])
+    slots = O.physical_slots(wl.block_table[b], np.arange(pos + 1), W.PAGE)
+    keys, ks = O.key_rows(idx["k"], idx.get("k_scale"), slots)
+    q = idx["q"][t]
+    if q.dtype == np.uint8:
+        qv = O.decode_e4m3(q)
+        qs = np.full(q.shape[0], float(idx["q_scale"][t]))
+    else:
+        qv, qs = q.astype(np.float64), np.ones(q.shape[0])
+    return O.index_scores_row(np.abs(qv), qs, np.abs(idx["w"][t].astype(np.float64)), np.abs(keys), ks)
+
+
+def check_scores(wl, rows, got: np.ndarray, exp: dict):
+    eps = SCORE_EPS[wl.cfg["idx_dtype"]]
+    worst = 0.0
+    for i, t in enumerate(rows):
+        n = int(wl.q_pos[t]) + 1
+        o = exp[t].astype(np.float64)
+        g = got[i, :n].astype(np.float64)
+        tol = SCORE_REL * np.abs(o) + eps * score_bound_row(wl, t)
+        err = np.abs(g - o)
+        bad = np.nonzero(~(err <= tol))[0]
+        assert bad.size == 0, f"row {t}: {bad.size} scores out of tolerance, first s={bad[0]} g={g[bad[0]]} o={o[bad[0]]}"
+        worst = max(worst, float(np.max(err / np.maximum(tol, 1e-30))))
+    return worst
+
+
+def check_attention(kind, got_out, got_lse, exp: dict, rows):
+    atol, rtol = ATT_TOL[kind]
+    for i, t in enumerate(rows):
+        o, l = exp[t]
+        g = got_out[i].astype(np.float64)
+        bad = ~(np.abs(g - o) <= atol + rtol * np.abs(o))
+        assert not bad.any(), f"row {t}: {bad.sum()} outputs out of tolerance, max err {np.max(np.abs(g - o))}"
+        if got_lse is not None:
+            gl = got_lse[i].astype(np.float64)
+            fin = np.isfinite(l)
+            assert np.array_equal(fin, np.isfinite(gl)), f"row {t}: lse finiteness differs"
+            assert np.all(np.abs(gl[fin] - l[fin]) <= LSE_ATOL[kind] + 1e-4 * np.abs(l[fin])), f"row {t}: lse"
+
+
+def to_np_out(x: torch.Tensor) -> np.ndarray:
+    return x.float().cpu().numpy()
+
+
+def tie_band_ok(oracle_scores_row: np.ndarray, K: int, got_ids: np.ndarray, exp_ids: np.ndarray) -> bool:
+    """Index sets equal except for positions whose oracle score lies within
+    1e-3 relative of the K-th oracle score (exact zeros when that score is 0)."""
+    a = set(int(x) for x in got_ids if x >= 0)
+    b = set(int(x) for x in exp_ids if x >= 0)
+    if len(a) != len(b):
+        return False
+    diff = a ^ b
+    if not diff:
+        return True
+    sK = float(np.sort(oracle_scores_row.astype(np.float64))[::-1][min(K, len(oracle_scores_row)) - 1])
+    band = 1e-3 * abs(sK)
+    return all(abs(float(oracle_scores_row[j]) - sK) <= band for j in diff)
+
+
+def kind_of(wl):
+    return wl.cfg["kv_dtype"]

@@ -1,0 +1,255 @@
+"""GPU parity: each libsia entry point against the CPU oracle on the same
+seeded inputs, at sizes the oracle finishes in seconds (several tiles, ragged
+tails, short rows).  Full-size configurations are in test_gpu_fullsize.py."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_index_attention_amd import sia
+from sparse_index_attention_amd import workloads as W
+
+from gpu_support import (check_attention, check_scores, dev, kind_of, tie_band_ok, to_np_out, upload,
+                         workload)
+
+pytestmark = pytest.mark.gpu
+
+TINY = ["tiny_prefill", "decode_tiny", "prefill_tiny", "quant_decode_tiny", "quant_decode_tile128_tiny",
+        "cp_chunk_prefill_tiny", "decode_h64_tiny"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sia.lib()
+
+
+@functools.lru_cache(maxsize=16)
+def oracle_run(name):
+    wl = workload(name)
+    K = wl.cfg["K"]
+    sc = O.index_scores(wl.oracle_indexer(), wl.oracle_seq())
+    sel = O.topk(sc, K, 0)
+    att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), sel, wl.softmax_scale)
+    return sc, sel, att
+
+
+def ld_of(wl):
+    return (wl.max_visible + 3) // 4 * 4
+
+
+@pytest.mark.parametrize("name", TINY)
+def test_index_scores(name):
+    wl = workload(name)
+    print(f"[scores] {name}", flush=True)
+    seq, ix, _, _ = upload(wl)
+    scores = sia.index_scores(ix, seq, ld=ld_of(wl))
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    sc, _, _ = oracle_run(name)
+    check_scores(wl, range(wl.Tq), got, sc)
+
+
+def oracle_score_buffer(wl, sc, fill=np.nan):
+    buf = np.full((wl.Tq, ld_of(wl)), fill, dtype=np.float32)
+    for t, row in sc.items():
+        buf[t, : row.shape[0]] = row
+    return buf
+
+
+@pytest.mark.parametrize("name", TINY)
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_bit_exact_on_oracle_scores(name, order):
+    wl = workload(name)
+    print(f"[topk] {name} order={order}", flush=True)
+    K = wl.cfg["K"]
+    seq, _, _, _ = upload(wl)
+    sc, _, _ = oracle_run(name)
+    buf = dev(oracle_score_buffer(wl, sc))          # NaN beyond q_pos: must never be read
+    idx, vals = sia.topk(buf, seq, K, order=order, with_vals=True)
+    torch.cuda.synchronize()
+    idx, vals = idx.cpu().numpy(), vals.cpu().numpy()
+    for t in range(wl.Tq):
+        exp = O.topk_row(sc[t], K, order)
+        assert np.array_equal(idx[t], exp), f"row {t}"
+        m = exp >= 0
+        assert np.all(vals[t][m] == sc[t][exp[m]]) and np.all(np.isneginf(vals[t][~m]))
+
+
+def _topk_rows_case(rows, K, order, max_visible=None):
+    T = len(rows)
+    n_max = max(len(r) for r in rows)
+    mv = max_visible or n_max
+    ld = (mv + 3) // 4 * 4
+    buf = np.full((T, ld), np.nan, dtype=np.float32)
+    for t, r in enumerate(rows):
+        buf[t, : len(r)] = r
+    pages = (mv + 63) // 64
+    seq = sia.SeqMap(dev(np.zeros(T, np.int32)), dev(np.array([len(r) - 1 for r in rows], np.int32)),
+                     dev(np.arange(pages, dtype=np.int32)[None]), pages, mv)
+    idx = sia.topk(dev(buf), seq, K, order=order)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for t, r in enumerate(rows):
+        exp = O.topk_row(r, K, order)
+        assert np.array_equal(idx[t], exp), f"case row {t} (n={len(r)}, K={K})"
+
+
+def _synthetic_rows(seed, ns):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i, n in enumerate(ns):
+        kind = i % 6
+        if kind == 0:
+            r = rng.standard_normal(n)
+        elif kind == 1:
+            r = np.round(rng.standard_normal(n) * 3)            # heavy ties
+        elif kind == 2:
+            r = np.where(rng.random(n) < 0.5, 0.0, -0.0)         # only signed zeros
+        elif kind == 3:
+            r = np.full(n, 7.25)                                  # all equal
+        elif kind == 4:
+            r = rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, size=n)   # wide range
+        else:
+            r = np.maximum(rng.standard_normal(n), 0)             # ReLU-like: many exact zeros
+        rows.append(r.astype(np.float32))
+    return rows
+
+
+@pytest.mark.parametrize("K", [1, 7, 64, 2048])
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_edge_cases_cached_rows(K, order):
+    print(f"[topk-edge] K={K} order={order}", flush=True)
+    ns = [1, 2, 5, 63, 64, 65, 1000, 2047, 2048, 2049, 5000, 32768, 12345, 3, 4096, 30000, 777, 2100]
+    _topk_rows_case(_synthetic_rows(K * 10 + order, ns), K, order)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_topk_long_rows_uncached(order):
+    print(f"[topk-long] order={order}", flush=True)
+    ns = [70000, 40000, 1, 2048, 65536, 100003]
+    _topk_rows_case(_synthetic_rows(99 + order, ns), 2048, order, max_visible=100003)
+
+
+@pytest.mark.parametrize("name", TINY)
+@pytest.mark.parametrize("entry", ["decode", "prefill"])
+def test_sparse_mla_on_oracle_indices(name, entry):
+    wl = workload(name)
+    print(f"[mla] {name} {entry}", flush=True)
+    K = wl.cfg["K"]
+    seq, _, q, kv = upload(wl)
+    _, sel, att = oracle_run(name)
+    idx = dev(np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32))
+    lse = torch.empty(wl.Tq, wl.cfg["H"], dtype=torch.float32, device="cuda")
+    fn = sia.sparse_mla_decode if entry == "decode" else sia.sparse_mla_prefill
+    out = fn(q, kv, seq, idx, K, wl.softmax_scale, lse=lse)
+    torch.cuda.synchronize()
+    check_attention(kind_of(wl), to_np_out(out), lse.cpu().numpy(), att, range(wl.Tq))
+
+
+@pytest.mark.parametrize("name", ["decode_tiny", "quant_decode_tiny", "prefill_tiny"])
+def test_sparse_mla_holes_and_permuted_lists(name):
+    """-1 holes anywhere in the list, positions in arbitrary order."""
+    wl = workload(name)
+    print(f"[mla-holes] {name}", flush=True)
+    K = wl.cfg["K"]
+    rng = np.random.default_rng(5)
+    _, sel, _ = oracle_run(name)
+    ids = np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32)
+    for t in range(wl.Tq):
+        rng.shuffle(ids[t])
+        ids[t][rng.random(K) < 0.3] = -1
+    sel2 = {t: ids[t] for t in range(wl.Tq)}
+    att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), sel2, wl.softmax_scale)
+    seq, _, q, kv = upload(wl)
+    lse = torch.empty(wl.Tq, wl.cfg["H"], dtype=torch.float32, device="cuda")
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        out = fn(q, kv, seq, dev(ids), K, wl.softmax_scale, lse=lse)
+        torch.cuda.synchronize()
+        check_attention(kind_of(wl), to_np_out(out), lse.cpu().numpy(), att, range(wl.Tq))
+
+
+def test_sparse_mla_all_invalid_row_gives_zero_and_neg_inf():
+    wl = workload("decode_tiny")
+    K = wl.cfg["K"]
+    seq, _, q, kv = upload(wl)
+    ids = np.full((wl.Tq, K), -1, np.int32)
+    ids[1, 3] = 0
+    lse = torch.empty(wl.Tq, wl.cfg["H"], dtype=torch.float32, device="cuda")
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        out = fn(q, kv, seq, dev(ids), K, wl.softmax_scale, lse=lse)
+        torch.cuda.synchronize()
+        o, l = to_np_out(out), lse.cpu().numpy()
+        assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+        row0 = O.kv_rows(wl.oracle_kv(), O.physical_slots(wl.block_table[1], np.array([0]), 64))
+        assert np.allclose(o[1], np.broadcast_to(row0[:, :512], (wl.cfg["H"], 512)), atol=1e-2, rtol=1e-2)
+
+
+@pytest.mark.parametrize("name", TINY)
+def test_index_select_attend_end_to_end(name):
+    wl = workload(name)
+    print(f"[fused] {name}", flush=True)
+    K = wl.cfg["K"]
+    seq, ix, q, kv = upload(wl)
+    idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    lse = torch.empty(wl.Tq, wl.cfg["H"], dtype=torch.float32, device="cuda")
+    out = sia.index_select_attend(ix, q, kv, seq, K, wl.softmax_scale, order=0, idx_out=idx, lse=lse)
+    torch.cuda.synchronize()
+    sc, sel, att = oracle_run(name)
+    ids, o, l = idx.cpu().numpy(), to_np_out(out), lse.cpu().numpy()
+    matched = []
+    for t in range(wl.Tq):
+        assert tie_band_ok(sc[t], K, ids[t], sel[t]), f"row {t}: index sets differ beyond the tie band"
+        if set(ids[t]) == set(sel[t]):
+            matched.append(t)
+    assert len(matched) >= 0.9 * wl.Tq
+    check_attention(kind_of(wl), o[matched], l[matched], att, matched)
+
+
+def test_deterministic_reruns():
+    wl = workload("decode_tiny")
+    K = wl.cfg["K"]
+    seq, ix, q, kv = upload(wl)
+    res = []
+    for _ in range(2):
+        idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+        out = sia.index_select_attend(ix, q, kv, seq, K, wl.softmax_scale, idx_out=idx)
+        torch.cuda.synchronize()
+        res.append((idx.cpu().numpy(), out.view(torch.int16).cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+def test_permuted_block_table_matches_identity():
+    """Moving pages around the pool (and the table with them) changes nothing."""
+    wl = workload("prefill_tiny")
+    K = wl.cfg["K"]
+    seq, ix, q, kv = upload(wl)
+    idx_a = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    out_a = sia.index_select_attend(ix, q, kv, seq, K, wl.softmax_scale, idx_out=idx_a)
+    tbl = wl.block_table[0]
+    ix2 = sia.Indexer(ix.q, ix.w, dev(wl.ik[tbl]), ix.q_scale, dev(wl.ik_scale[tbl]))
+    kv2 = sia.LatentKV(dev(wl.kv[tbl]), 512, 64)
+    seq2 = sia.SeqMap(seq.q_seq, seq.q_pos, dev(np.arange(len(tbl), dtype=np.int32)[None]), len(tbl),
+                      wl.max_visible)
+    idx_b = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    out_b = sia.index_select_attend(ix2, q, kv2, seq2, K, wl.softmax_scale, idx_out=idx_b)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_b)
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+
+
+def test_split_count_invariance():
+    """Decode (rows split over workgroups, merged by LSE) equals prefill (one
+    workgroup per token) within fp32 rounding of the merge."""
+    wl = workload("decode_tiny")
+    K = wl.cfg["K"]
+    seq, _, q, kv = upload(wl)
+    _, sel, _ = oracle_run("decode_tiny")
+    idx = dev(np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32))
+    a = sia.sparse_mla_decode(q, kv, seq, idx, K, wl.softmax_scale).float()
+    b = sia.sparse_mla_prefill(q, kv, seq, idx, K, wl.softmax_scale).float()
+    torch.cuda.synchronize()
+    assert torch.allclose(a, b, atol=1e-2, rtol=1e-2)
