@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = the whole hot path (indexer scores -> Top-K -> sparse
+MLA) over one batch of synthetic input, on one GPU.
+
+Default workload: decode, batch 64, context 32768 per sequence, indexer 64 heads
+x 128 fp8, Top-K 2048, MLA 128 heads x (512 + 64) bf16, paged cache with 64-token
+pages and shuffled block tables.  Inputs are resident in HBM before timing; the
+timed loop rotates over `--copies` distinct device copies of them so that no
+step is served from the previous step's Infinity Cache contents.
+
+Prints one JSON line (see the keys below).  `--gpus N` with N > 1 is refused:
+this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/s for index+TopK+sparse-MLA; decode µs/step; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill"])
+    p.add_argument("--copies", type=int, default=3, help="distinct device copies of the inputs (decode)")
+    p.add_argument("--order", type=int, default=0, help="Top-K output order (0 score-sorted, 1 by position)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-breakdown", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic_work(wl):
+    """Bytes / flops per launch of each kernel, from the method's definition
+    (inputs read once, outputs written once; the score round trip and split
+    partials are not algorithmic)."""
+    c = wl.cfg
+    Hi, Di, H, Dc, Dr, K = c["Hi"], c["Di"], c["H"], c["Dc"], c["Dr"], c["K"]
+    vis = (wl.q_pos.astype("int64") + 1)
+    sel = vis.clip(max=K)
+    key_b = Di + 4 if c["idx_dtype"] == "fp8" else 4 * Di
+    q_b = Hi * Di * (1 if c["idx_dtype"] == "fp8" else 4) + 4 * Hi + 4
+    if c["kv_dtype"] == "bf16":
+        row_b = 2 * (Dc + Dr)
+    elif c["kv_dtype"] == "fp8":
+        row_b = Dc + 2 * Dr + 4 * (1 if c["kv_scale"] == (1, 128) else 0)
+    else:
+        row_b = 4 * (Dc + Dr)
+    elt = 4 if c["kv_dtype"] == "f32" else 2
+    idx_bytes = float(vis.sum() * key_b + wl.Tq * q_b)
+    idx_flops = float(vis.sum() * 2 * Hi * Di)
+    mla_bytes = float(sel.sum() * (row_b + 4) + wl.Tq * H * ((Dc + Dr) + Dc) * elt)
+    mla_flops = float(sel.sum() * 2 * H * ((Dc + Dr) + Dc))
+    return {"index_scores": (idx_bytes, idx_flops), "topk": (float(wl.Tq * K * 4), 0.0),
+            "sparse_mla": (mla_bytes, mla_flops)}
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    K = wl.cfg["K"]
+    rows = list(np.argsort(-wl.q_pos, kind="stable")) if wl.cfg["kind"] != "decode" else list(range(wl.Tq))
+    rng = np.random.default_rng(0)
+    if wl.cfg["kind"] != "decode":
+        rows = list(rng.choice(wl.Tq, size=min(wl.Tq, 64), replace=False))
+    done, t0 = [], time.perf_counter()
+    for t in rows:
+        O.index_select_attend(wl.oracle_indexer(), wl.q, wl.oracle_kv(), wl.oracle_seq(), K, wl.softmax_scale,
+                              rows=[int(t)])
+        done.append(int(t))
+        if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
+            break
+    el = time.perf_counter() - t0
+    vis_done = float(sum(int(wl.q_pos[t]) + 1 for t in done))
+    vis_all = float((wl.q_pos.astype("int64") + 1).sum())
+    rate = len(done) / el
+    kind = "oracle"
+    sample = f"{len(done)} of {wl.Tq} query tokens of the '{wl.name}' workload, whole path in float64"
+    if wl.cfg["kind"] != "decode":
+        # prefill rows differ in cost: scale by visible-key count
+        rate = wl.Tq / (el * vis_all / vis_done)
+        sample += "; rate extrapolated by visible-key count"
+    return {"value": rate, "unit": "query tokens/s", "cores": int(cores), "kind": kind, "sample": sample,
+            "seconds": round(el, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design note, "
+              "not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_index_attention_amd import sia
+    from sparse_index_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sia.lib()
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    t_gen = time.perf_counter()
+    wl = W.make_workload(args.workload)
+    c = wl.cfg
+    K, H = c["K"], c["H"]
+    print(f"[bench] generated in {time.perf_counter() - t_gen:.1f}s; uploading", file=sys.stderr, flush=True)
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    decode = c["kind"] == "decode"
+    copies = max(1, args.copies) if decode else 1
+    sets = []
+    base = None
+    for i in range(copies):
+        if base is None:
+            seq = sia.SeqMap(dev(wl.q_seq), dev(wl.q_pos), dev(wl.block_table), wl.num_pages, wl.max_visible)
+            if c["idx_dtype"] == "f32":
+                ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik))
+            else:
+                ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik), dev(wl.iq_scale), dev(wl.ik_scale))
+            if c["kv_dtype"] == "fp8":
+                kv = sia.LatentKV(dev(wl.kv), c["Dc"], c["Dr"], dev(wl.kv_scale), *c["kv_scale"])
+            else:
+                kv = sia.LatentKV(dev(wl.kv), c["Dc"], c["Dr"])
+            q = dev(wl.q)
+            base = (seq, ix, q, kv)
+        else:
+            seq, ix, q, kv = base
+            ix = sia.Indexer(ix.q.clone(), ix.w.clone(), ix.k_pool.clone(),
+                             None if ix.q_scale is None else ix.q_scale.clone(),
+                             None if ix.k_scale is None else ix.k_scale.clone())
+            kv = sia.LatentKV(kv.pool.clone(), kv.latent_dim, kv.rope_dim,
+                              None if kv.scale is None else kv.scale.clone(), kv.scale_tokens, kv.scale_elems)
+            q = q.clone()
+            seq = sia.SeqMap(seq.q_seq.clone(), seq.q_pos.clone(), seq.block_table.clone(), seq.num_pages,
+                             seq.max_visible)
+        n_ws = sia.workspace_size(sia.OP_INDEX_SELECT_ATTEND, seq, K, H, c["Dc"])
+        ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+        out = torch.empty(wl.Tq, H, c["Dc"], dtype=q.dtype, device="cuda")
+        idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+        sets.append(dict(seq=seq, ix=ix, q=q, kv=kv, ws=ws, out=out, idx=idx))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = sets[i % copies]
+        sia.index_select_attend(s["ix"], s["q"], s["kv"], s["seq"], K, wl.softmax_scale, order=args.order,
+                                idx_out=s["idx"], out=s["out"], ws=s["ws"], stream=stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("[bench] timing", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    value = wl.Tq / (ms_per_step / 1e3)
+
+    # per-kernel breakdown, measured live with events on the launch stream
+    work = algorithmic_work(wl)
+    breakdown = {}
+    if not args.no_breakdown:
+        ld = (wl.max_visible + 63) // 64 * 64
+        scores = [torch.empty(wl.Tq, ld, dtype=torch.float32, device="cuda") for _ in range(copies)]
+        nmla = sia.workspace_size(sia.OP_MLA_DECODE, sets[0]["seq"], K, H, c["Dc"]) if c["kv_dtype"] != "f32" else 0
+        mws = torch.empty(max(nmla, 1), dtype=torch.uint8, device="cuda")
+        mla_fn = sia.sparse_mla_decode if sia.workspace_size(sia.OP_MLA_DECODE, sets[0]["seq"], K, H, c["Dc"]) > 0 \
+            else sia.sparse_mla_prefill
+        names = ["index_scores", "topk", "sparse_mla"]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.warmup + args.steps):
+            s = sets[i % copies]
+            rec = ev[i - args.warmup] if i >= args.warmup else None
+            if rec:
+                rec[0].record(stream)
+            sia.index_scores(s["ix"], s["seq"], scores[i % copies], stream=stream)
+            if rec:
+                rec[1].record(stream)
+            sia.topk(scores[i % copies], s["seq"], K, order=args.order, idx=s["idx"], stream=stream)
+            if rec:
+                rec[2].record(stream)
+            mla_fn(s["q"], s["kv"], s["seq"], s["idx"], K, wl.softmax_scale, out=s["out"], ws=mws, stream=stream)
+            if rec:
+                rec[3].record(stream)
+        torch.cuda.synchronize()
+        for k, nm in enumerate(names):
+            us = 1e3 * sum(r[k].elapsed_time(r[k + 1]) for r in ev) / args.steps
+            breakdown[nm] = round(us, 2)
+        del scores
+
+    roofline = None
+    if breakdown:
+        dom = max(("index_scores", "sparse_mla"), key=lambda n: breakdown[n])
+        by, fl = work[dom]
+        us = breakdown[dom]
+        if decode:
+            achieved = by / (us * 1e-6) / 1e9
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "algorithmic_bytes": by, "avg_us": us}
+        else:
+            peak = FP8_PEAK_TFLOPS if dom == "index_scores" else BF16_PEAK_TFLOPS
+            achieved = fl / (us * 1e-6) / 1e12
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                        "algorithmic_flops": fl, "avg_us": us}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    cfg = {"workload": args.workload, "queries": wl.Tq, "K": K, "indexer": f"{c['Hi']}x{c['Di']} {c['idx_dtype']}",
+           "mla": f"{H} heads, {c['Dc']}+{c['Dr']} {c['kv_dtype']}", "page_size": 64, "topk_order": args.order,
+           "input_copies": copies}
+    if decode:
+        cfg.update(batch=int(len(wl.seq_lens)), context=int(wl.seq_lens.max()))
+    else:
+        cfg.update(max_visible=wl.max_visible)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2), "wall_s": round(wall, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16" if c["idx_dtype"] == "fp8" else "f32", "data": "synthetic",
+        "config": cfg, "breakdown_us": breakdown, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -162,7 +162,7 @@ int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, 
  *   out   [T, heads, latent] in q's dtype;  lse [T, heads] float or NULL
  *   idx   [T, K] int32 (-1 = unused slot)
  * Supported: f32 cache with heads <= 64; bf16/fp8 cache with heads in
- * {32, 64, 128}.  K >= 1.
+ * {32, 64, 128}.  1 <= K <= 2048.
  * _decode splits each token's rows over several workgroups and merges the
  * partial results in a fixed order (needs workspace, see sia_workspace_size);
  * _prefill gives each token one workgroup (no workspace; ws may be NULL).      */

@@ -71,6 +71,7 @@ static int check_kv(const sia_kv_in* kv, sia_dtype q_dtype, int heads, int K) {
     return SIA_OK;
   }
   if (kv->dtype != SIA_BF16 && kv->dtype != SIA_FP8_E4M3) return SIA_ERR_UNSUPPORTED;
+  if (K > 2048) return SIA_ERR_UNSUPPORTED;
   if (q_dtype != SIA_BF16) return SIA_ERR_UNSUPPORTED;
   if (kv->latent_dim != 512 || kv->rope_dim != 64) return SIA_ERR_UNSUPPORTED;
   if (heads != 32 && heads != 64 && heads != 128) return SIA_ERR_UNSUPPORTED;

@@ -151,27 +151,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 128-byte chunk group), and every LDS read is one per-lane base register plus a
 // compile-time immediate.
 //
-// The first QREG K-steps of the query operand stay in registers; the rest is
-// parked in LDS (per wave, one 16-byte slot per lane and step) to leave room for
-// the 256-register output accumulator.
-template <bool FP8> struct MlaCfg { static constexpr int QREG = FP8 ? 16 : 18; };
+// Each workgroup produces one half of the 512 latent output columns (VH = 256).
+// Both halves of a (token, split) recompute the scores S^T; in exchange a wave's
+// output accumulator is 128 registers, which leaves room for the whole query
+// operand in registers and for operand prefetching.  Blocks b and b + 8 (the two
+// halves) are scheduled on the same XCD so the second gather is served by its L2.
+constexpr int kVH = 256;
+constexpr int kBufs = 3;                 // gather ring: tiles i+1 and i+2 in flight while i is used
+constexpr int kMaxSplitRows = 2048;      // rows of one split, slots resolved once per workgroup
+constexpr int kVT = kVH / 32;  // 32-column output tiles per half
+
+// direct global->LDS loads each lane issues per bf16 tile
+template <int NW> constexpr int kBf16LoadsPerTile() { return 9 * ((4 + NW - 1) / NW); }
 
 template <int NW, bool FP8>
 __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int QREG = MlaCfg<FP8>::QREG, QLDS = 36 - QREG;
   constexpr int TPR = NT / kRowsTile;          // threads per row in the fp8 gather
   constexpr int kFp8Loads = 40 / TPR;          // 640-byte rows = 40 loads of 16 bytes
-  __shared__ __attribute__((aligned(16))) unsigned char tile[2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char qlds[NW * QLDS * 64 * 16];
-  __shared__ int32_t sslot[3][kRowsTile];
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kBufs * kTileBytes];
+  __shared__ int32_t sslot[kMaxSplitRows];
+
+  // block -> (token, split, column half); b and b+8 share (token, split)
+  const int bid = blockIdx.x;
+  const int grp = bid >> 4, within = bid & 15;
+  const int vhalf = within >> 3;
+  const int unit = grp * 8 + (within & 7);     // token * splits + split
+  if (unit >= a.s.T * a.splits) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, nn = lane & 31;
   lds_u8* const tl = (lds_u8*)tile;
-  lds_u8* const ql = (lds_u8*)qlds + wave * (QLDS * 64 * 16) + lane * 16;
-  const int split = blockIdx.x % a.splits;
-  const int t = blockIdx.x / a.splits;
+  const int split = unit % a.splits;
+  const int t = unit / a.splits;
   const int j0 = split * a.rows_per_split;
   int j1 = j0 + a.rows_per_split;
   j1 = j1 < a.K ? j1 : a.K;
@@ -183,26 +195,24 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   const int head = wave * 32 + nn;
   const unsigned char* kvb = (const unsigned char*)a.kv;
 
-  // slot numbers of tile i's rows (-1: no row)
-  auto fill_slots = [&](int i) {
-    if (tid < kRowsTile) {
-      const int j = j0 + i * kRowsTile + tid;
-      int slot = -1;
-      if (j < j1) {
-        const int p = irow[j];
-        if (p >= 0 && p < a.s.max_visible) slot = (int)page_slot(table, p, a.s.num_pages);
-      }
-      sslot[i % 3][tid] = slot;
+  // physical slots of all rows of this split (-1: no row), resolved once
+  for (int r = tid; r < ntiles * kRowsTile; r += NT) {
+    const int j = j0 + r;
+    int slot = -1;
+    if (j < j1) {
+      const int p = irow[j];
+      if (p >= 0 && p < a.s.max_visible) slot = (int)page_slot(table, p, a.s.num_pages);
     }
-  };
+    sslot[r] = slot;
+  }
 
   // ---- gather: bf16 rows go global -> LDS directly --------------------------
   // wave instruction (row group rg, chunk group m) covers rows 8rg..8rg+7 and
   // chunks 8m..8m+7; lane L: row 8rg + L/8, chunk 8m + ((L%8) ^ swz(row)).
   const int g_sub = lane & 7;
   auto issue_bf16 = [&](int i) {
-    const int32_t* ss = sslot[i % 3];
-    lds_u8* dst = tl + (i & 1) * kTileBytes;
+    const int32_t* ss = sslot + i * kRowsTile;
+    lds_u8* dst = tl + (i % kBufs) * kTileBytes;
 #pragma unroll
     for (int rg = wave; rg < 4; rg += NW) {
       const int r = 8 * rg + (lane >> 3);
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   float stage_scale[FP8 ? kFp8Loads : 1];
   const int f_row = tid / TPR, f_sub = tid % TPR;
   auto issue_fp8 = [&](int i) {
-    const int32_t* ss = sslot[i % 3];
+    const int32_t* ss = sslot + i * kRowsTile;
     const int slot = ss[f_row] >= 0 ? ss[f_row] : 0;
     const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
     const int page = slot >> 6, tok = slot & 63;
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     }
   };
   auto commit_fp8 = [&](int i) {
-    lds_u8* dst = tl + (i & 1) * kTileBytes;
+    lds_u8* dst = tl + (i % kBufs) * kTileBytes;
     const int r = f_row, sw = swz(r);
 #pragma unroll
     for (int m = 0; m < kFp8Loads; ++m) {
@@ -263,13 +273,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   };
 
   // ---- query operand: Q^T[depth, head], lane (hh, nn): head nn, chunk 2i + hh
-  v8bf qb[QREG];
+  v8bf qb[36];
   {
     const v8bf* qr = (const v8bf*)((const uint16_t*)a.q + ((int64_t)t * a.H + head) * kD);
 #pragma unroll
-    for (int i = 0; i < QREG; ++i) qb[i] = qr[2 * i + hh];
-#pragma unroll
-    for (int i = QREG; i < 36; ++i) *(lds_v8bf*)(ql + (i - QREG) * 1024) = qr[2 * i + hh];
+    for (int i = 0; i < 36; ++i) qb[i] = qr[2 * i + hh];
   }
 
   // per-lane LDS read bases (see the layout note above)
@@ -285,42 +293,51 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   int vbase[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
-    vbase[par] = 128 * vrow0 + 16 * ((4 * par + 2 * (g & 1) + (qd >> 1)) ^ vsw) + 8 * (qd & 1);
+    vbase[par] = 128 * vrow0 + 16 * ((4 * par + 2 * (g & 1) + (qd >> 1)) ^ vsw) + 8 * (qd & 1) +
+                 4096 * 4 * vhalf;   // column half: chunk groups 4..7
 
-  v16f o[16];
+  v16f o[kVT];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) o[v] = v16f{};
+  for (int v = 0; v < kVT; ++v) o[v] = v16f{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // prologue: tile 0 (and tile 1 for bf16) in flight
+  __syncthreads();
   if (ntiles > 0) {
-    fill_slots(0);
-    __syncthreads();
     if constexpr (FP8) {
       issue_fp8(0);
       commit_fp8(0);
     } else {
       issue_bf16(0);
+      if (ntiles > 1) issue_bf16(1);
     }
-    if (ntiles > 1) fill_slots(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
 
   for (int i = 0; i < ntiles; ++i) {
+    // bf16: tile i's loads are complete once at most one tile (i+1) is outstanding
+    if constexpr (!FP8) {
+      if (i + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBf16LoadsPerTile<NW>()) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
     if (i + 1 < ntiles) {
       if constexpr (FP8) issue_fp8(i + 1);
-      else issue_bf16(i + 1);
+      else if (i + 2 < ntiles) issue_bf16(i + 2);
     }
-    lds_u8* cur = tl + (i & 1) * kTileBytes;
-    const int32_t* ss = sslot[i % 3];
+    lds_u8* cur = tl + (i % kBufs) * kTileBytes;
+    const int32_t* ss = sslot + i * kRowsTile;
 
-    // S^T = KV . Q^T  (rows x heads)
+    // S^T = KV . Q^T  (rows x heads); operands are loaded PF steps ahead
+    constexpr int PF = 3;
     v16f sacc = {};
+    v8bf kring[PF];
+#pragma unroll
+    for (int st = 0; st < PF; ++st) kring[st] = *(lds_v8bf*)(cur + sbase[st & 3] + 4096 * (st >> 2));
 #pragma unroll
     for (int st = 0; st < 36; ++st) {
-      const v8bf kf = *(lds_v8bf*)(cur + sbase[st & 3] + 4096 * (st >> 2));
-      const v8bf qf = st < QREG ? qb[st < QREG ? st : 0] : *(lds_v8bf*)(ql + (st - QREG) * 1024);
-      sacc = mfma_bf16(kf, qf, sacc);
+      const v8bf kf = kring[st % PF];
+      if (st + PF < 36) kring[st % PF] = *(lds_v8bf*)(cur + sbase[(st + PF) & 3] + 4096 * ((st + PF) >> 2));
+      sacc = mfma_bf16(kf, qb[st], sacc);
     }
     // online softmax over the tile's rows (log2 domain); lane owns head nn,
     // rows 8*(r/4) + 4*hh + r%4
@@ -341,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
+      for (int v = 0; v < kVT; ++v)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[v][r] *= alpha;
     }
@@ -355,36 +372,39 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     }
     l_run += psum;
 
-    // O^T += V^T . P^T ; MFMA mf covers tile rows 16mf + R(hh, jj)
+    // O^T += V^T . P^T ; MFMA mf covers tile rows 16mf + R(hh, jj); operands one step ahead
+    auto vfrag = [&](int vt, int mf) -> v8bf {
+      const int imm = 4096 * (vt >> 1) + 2048 * mf;
+      const v4bf x0 = lds_tr16(cur, vbase[vt & 1] + imm);
+      const v4bf x1 = lds_tr16(cur, vbase[vt & 1] + imm + 1024);
+      return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    v8bf vring[PF];
 #pragma unroll
-    for (int vt = 0; vt < 16; ++vt) {
+    for (int k = 0; k < PF; ++k) vring[k] = vfrag(k >> 1, k & 1);
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf) {
-        const int imm = 4096 * (vt >> 1) + 2048 * mf;
-        const v4bf x0 = lds_tr16(cur, vbase[vt & 1] + imm);
-        const v4bf x1 = lds_tr16(cur, vbase[vt & 1] + imm + 1024);
-        const v8bf af = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[vt] = mfma_bf16(af, pb[mf], o[vt]);
-      }
+    for (int k = 0; k < 2 * kVT; ++k) {
+      const int vt = k >> 1, mf = k & 1;
+      const v8bf af = vring[k % PF];
+      if (k + PF < 2 * kVT) vring[k % PF] = vfrag((k + PF) >> 1, (k + PF) & 1);
+      o[vt] = mfma_bf16(af, pb[mf], o[vt]);
     }
 
-    if (i + 2 < ntiles) fill_slots(i + 2);
     if constexpr (FP8) {
-      // the other buffer was last read in iteration i-1, before the previous barrier
+      // buffer (i+1) % kBufs was last read two iterations ago, before the barrier above
       if (i + 1 < ntiles) commit_fp8(i + 1);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
 
-  // ---- finish: normalise and write
+  // ---- finish: normalise and write this column half
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  const int vc0 = kVH * vhalf;
   if (a.splits == 1) {
-    uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + head) * kDc;
+    uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + head) * kDc + vc0;
 #pragma unroll
-    for (int vt = 0; vt < 16; ++vt)
+    for (int vt = 0; vt < kVT; ++vt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int vc = 32 * vt + 8 * q4 + 4 * hh;
@@ -393,19 +413,19 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         w.y = pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv);
         *(uint2*)(out + vc) = w;
       }
-    if (a.lse && hh == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
+    if (a.lse && hh == 0 && vhalf == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
   } else {
     const int64_t pidx = ((int64_t)t * a.splits + split) * a.H + head;
-    float* po = a.ws_o + pidx * kDc;
+    float* po = a.ws_o + pidx * kDc + vc0;
 #pragma unroll
-    for (int vt = 0; vt < 16; ++vt)
+    for (int vt = 0; vt < kVT; ++vt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int vc = 32 * vt + 8 * q4 + 4 * hh;
         *(float4*)(po + vc) = make_float4(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv, o[vt][4 * q4 + 2] * inv,
                                           o[vt][4 * q4 + 3] * inv);
       }
-    if (hh == 0) a.ws_lse[pidx] = lse_v;
+    if (hh == 0 && vhalf == 0) a.ws_lse[pidx] = lse_v;
   }
 }
 
@@ -450,10 +470,12 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
 int mla_splits(int T, int K, int heads) {
   if (T <= 0) return 1;
   const int cus = num_cus();
-  int s = (cus + T - 1) / T;             // about one workgroup per CU
+  int s = (cus / 2 + T - 1) / T;         // two column-half workgroups per unit: ~one per CU
+  const int min_s = (K + kMaxSplitRows - 1) / kMaxSplitRows;   // a split holds at most kMaxSplitRows rows
   const int max_s = (K + kRowsTile * 2 - 1) / (kRowsTile * 2);  // keep >= 2 tiles per split
   s = s > max_s ? max_s : s;
   s = s > 32 ? 32 : s;
+  s = s < min_s ? min_s : s;
   return s < 1 ? 1 : s;
 }
 
@@ -494,7 +516,8 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
     a.ws_o = (float*)ws;
     a.ws_lse = a.ws_o + (size_t)s.T * a.splits * heads * kDc;
   }
-  const dim3 grid((unsigned)((int64_t)s.T * a.splits));
+  const int64_t units = (int64_t)s.T * a.splits;
+  const dim3 grid((unsigned)(((units + 7) / 8) * 16));
   const bool fp8 = kv.dtype == SIA_FP8_E4M3;
 #define SIA_LAUNCH_MLA(NW)                                                                   \
   if (fp8)                                                                                   \
