@@ -14,10 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsia.so")
 SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "sia_api.cpp"]
-# per-source extra flags: the attention kernel keeps its MFMA accumulators in the
-# VGPR file (AGPRs then serve as register-to-register spill space), which avoids
-# scratch spills for its 256-register output tile.
-SOURCE_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source extra flags (none needed at present)
+SOURCE_FLAGS = {}
 
 
 def hipcc() -> str:

@@ -159,7 +159,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kVH = 256;
 constexpr int kBufs = 3;                 // gather ring: tiles i+1 and i+2 in flight while i is used
 constexpr int kMaxSplitRows = 2048;      // rows of one split, slots resolved once per workgroup
+// The query operand's first kQReg K-steps stay in registers, the last kQLds are
+// read from LDS (one 16-byte slot per lane and step); this keeps the register
+// allocator from shuffling the operand through AGPRs.
+constexpr int kQLds = 10, kQReg = 36 - kQLds;
 constexpr int kVT = kVH / 32;  // 32-column output tiles per half
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt = n (bits 3:0 and 15:14),
+// expcnt = 7 (no wait), lgkmcnt = 0
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N)); }
+// Nine 16-byte direct loads of one row group (chunk groups m = 0..8 of 8 rows):
+// global src + 128*m -> LDS dst + 4096*m, all from one address register pair.
+template <int M>
+__device__ __forceinline__ void dma_row(const unsigned char* src, lds_u8* dst) {
+  if constexpr (M < 9) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 4096 * M - 128 * M), 16, 128 * M, 0);
+    dma_row<M + 1>(src, dst);
+  }
+}
+// Keeps a value's registers allocated up to this point (emits no instruction).
+__device__ __forceinline__ void keep_live(const void* p) { asm volatile("" ::"v"(p)); }
 
 // direct global->LDS loads each lane issues per bf16 tile
 template <int NW> constexpr int kBf16LoadsPerTile() { return 9 * ((4 + NW - 1) / NW); }
@@ -169,8 +189,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   constexpr int NT = NW * 64;
   constexpr int TPR = NT / kRowsTile;          // threads per row in the fp8 gather
   constexpr int kFp8Loads = 40 / TPR;          // 640-byte rows = 40 loads of 16 bytes
-  __shared__ __attribute__((aligned(16))) unsigned char tile[kBufs * kTileBytes];
-  __shared__ int32_t sslot[kMaxSplitRows];
+  // three distinct LDS objects (not one array): the compiler then sees that the
+  // in-flight direct loads into one buffer cannot alias reads of another and
+  // does not drain them before every tile
+  __shared__ __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tile2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) int32_t sslot[kMaxSplitRows + 2 * kRowsTile];
+  __shared__ __attribute__((aligned(16))) unsigned char qlds[NW * kQLds * 64 * 16];
 
   // block -> (token, split, column half); b and b+8 share (token, split)
   const int bid = blockIdx.x;
@@ -181,7 +207,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, nn = lane & 31;
-  lds_u8* const tl = (lds_u8*)tile;
   const int split = unit % a.splits;
   const int t = unit / a.splits;
   const int j0 = split * a.rows_per_split;
@@ -196,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   const unsigned char* kvb = (const unsigned char*)a.kv;
 
   // physical slots of all rows of this split (-1: no row), resolved once
-  for (int r = tid; r < ntiles * kRowsTile; r += NT) {
+  for (int r = tid; r < (ntiles + 2) * kRowsTile; r += NT) {
     const int j = j0 + r;
     int slot = -1;
     if (j < j1) {
@@ -210,18 +235,31 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   // wave instruction (row group rg, chunk group m) covers rows 8rg..8rg+7 and
   // chunks 8m..8m+7; lane L: row 8rg + L/8, chunk 8m + ((L%8) ^ swz(row)).
   const int g_sub = lane & 7;
-  auto issue_bf16 = [&](int i) {
+  // All nine loads of a row group share one address register pair: chunk group m
+  // is reached through the instruction offset 128*m, which the hardware adds to
+  // both the global and the LDS address, so the LDS base is pre-compensated.  The
+  // pair is returned so that the caller keeps it allocated while the loads are in
+  // flight (a load into LDS counts as a store whose address is read late; reusing
+  // the registers would make the compiler drain every outstanding load).
+  constexpr int kRG = (4 + NW - 1) / NW;   // 8-row groups per wave
+  struct Held { const unsigned char* p[kRG]; };
+  auto issue_bf16 = [&](int i, lds_u8* dst) __attribute__((always_inline)) -> Held {
     const int32_t* ss = sslot + i * kRowsTile;
-    lds_u8* dst = tl + (i % kBufs) * kTileBytes;
+    Held h;
 #pragma unroll
-    for (int rg = wave; rg < 4; rg += NW) {
+    for (int k = 0; k < kRG; ++k) {
+      const int rg = wave + NW * k;
       const int r = 8 * rg + (lane >> 3);
       const int slot = ss[r] >= 0 ? ss[r] : 0;
       const unsigned char* src = kvb + (int64_t)slot * (kD * 2) + 16 * (g_sub ^ swz(r));
-#pragma unroll
-      for (int m = 0; m < 9; ++m)
-        __builtin_amdgcn_global_load_lds(src + 128 * m, (lds_void*)(dst + (m * 256 + 64 * rg) * 16), 16, 0, 0);
+      h.p[k] = src;
+      dma_row<0>(src, dst + 64 * rg * 16);
     }
+    return h;
+  };
+  auto keep = [&](const Held& h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kRG; ++k) keep_live(h.p[k]);
   };
 
   // ---- gather: fp8 rows go through registers and are dequantized to bf16 ----
@@ -229,7 +267,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   v4i stage[FP8 ? kFp8Loads : 1];
   float stage_scale[FP8 ? kFp8Loads : 1];
   const int f_row = tid / TPR, f_sub = tid % TPR;
-  auto issue_fp8 = [&](int i) {
+  auto issue_fp8 = [&](int i) __attribute__((always_inline)) {
     const int32_t* ss = sslot + i * kRowsTile;
     const int slot = ss[f_row] >= 0 ? ss[f_row] : 0;
     const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
@@ -243,8 +281,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       stage_scale[m] = c < 32 ? a.kv_scale[sbase + (16 * c) / a.scale_elems] : 1.f;
     }
   };
-  auto commit_fp8 = [&](int i) {
-    lds_u8* dst = tl + (i % kBufs) * kTileBytes;
+  auto commit_fp8 = [&](lds_u8* dst) __attribute__((always_inline)) {
     const int r = f_row, sw = swz(r);
 #pragma unroll
     for (int m = 0; m < kFp8Loads; ++m) {
@@ -273,11 +310,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   };
 
   // ---- query operand: Q^T[depth, head], lane (hh, nn): head nn, chunk 2i + hh
-  v8bf qb[36];
+  v8bf qb[kQReg];
+  lds_u8* const ql = (lds_u8*)qlds + wave * (kQLds * 64 * 16) + lane * 16;
   {
     const v8bf* qr = (const v8bf*)((const uint16_t*)a.q + ((int64_t)t * a.H + head) * kD);
 #pragma unroll
-    for (int i = 0; i < 36; ++i) qb[i] = qr[2 * i + hh];
+    for (int i = 0; i < kQReg; ++i) qb[i] = qr[2 * i + hh];
+#pragma unroll
+    for (int i = kQReg; i < 36; ++i) *(lds_v8bf*)(ql + (i - kQReg) * 1024) = qr[2 * i + hh];
+    // keep the operand resident: without this the compiler re-loads it from
+    // memory inside the tile loop to save registers
+#pragma unroll
+    for (int i = 0; i < kQReg; ++i) asm volatile("" : "+v"(qb[i]));
   }
 
   // per-lane LDS read bases (see the layout note above)
@@ -301,43 +345,84 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   for (int v = 0; v < kVT; ++v) o[v] = v16f{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  Held held_old{}, held_new{};   // address pairs of the two tiles whose loads may be in flight
+  lds_u8* const T0 = (lds_u8*)tile0;
+  lds_u8* const T1 = (lds_u8*)tile1;
+  lds_u8* const T2 = (lds_u8*)tile2;
   // prologue: tile 0 (and tile 1 for bf16) in flight
   __syncthreads();
   if (ntiles > 0) {
     if constexpr (FP8) {
       issue_fp8(0);
-      commit_fp8(0);
+      commit_fp8(T0);
     } else {
-      issue_bf16(0);
-      if (ntiles > 1) issue_bf16(1);
+      held_old = issue_bf16(0, T0);
+      held_new = issue_bf16(1, T1);   // unconditional, like the in-loop issues
     }
   }
 
-  for (int i = 0; i < ntiles; ++i) {
-    // bf16: tile i's loads are complete once at most one tile (i+1) is outstanding
+  // one tile: compute on `cur`; the loads of tile i+1 (fp8: committed into
+  // `nxt1`) or tile i+2 (bf16: straight into `nxt2`) overlap with it
+  auto tile_step = [&](int i, lds_u8* cur, lds_u8* nxt1, lds_u8* nxt2) __attribute__((always_inline)) {
+    // Tile i has landed once at most one later tile's direct loads are still in
+    // flight (bf16), and every wave's LDS writes are done.  A plain s_barrier is
+    // used on purpose: __syncthreads() would also drain the loads of tile i+1.
+    // (the wait is a compiler-visible builtin so that its own bookkeeping of the
+    // in-flight direct loads stays exact)
+    // With the loads issued unconditionally, exactly one younger tile is always in flight.
     if constexpr (!FP8) {
-      if (i + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBf16LoadsPerTile<NW>()) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      keep(held_old);
+      keep(held_new);
+      wait_vm_lgkm0<kBf16LoadsPerTile<NW>()>();
+    } else {
+      wait_vm_lgkm0<63>();
     }
-    __syncthreads();
-    if (i + 1 < ntiles) {
-      if constexpr (FP8) issue_fp8(i + 1);
-      else if (i + 2 < ntiles) issue_bf16(i + 2);
+    asm volatile("s_barrier" ::: "memory");
+    if constexpr (FP8) {
+      if (i + 1 < ntiles) issue_fp8(i + 1);
+    } else {
+      // unconditional (past the end it re-reads row 0 into a finished buffer), so
+      // the compiler keeps the load's LDS target known and does not drain it
+      held_old = held_new;          // tile i's loads have landed: its pair is free
+      held_new = issue_bf16(i + 2, nxt2);
     }
-    lds_u8* cur = tl + (i % kBufs) * kTileBytes;
     const int32_t* ss = sslot + i * kRowsTile;
 
-    // S^T = KV . Q^T  (rows x heads); operands are loaded PF steps ahead
-    constexpr int PF = 3;
-    v16f sacc = {};
-    v8bf kring[PF];
+    // validity of this lane's 16 rows: rows 8k + 4hh + 0..3 are four consecutive slots
+    int4 vflag[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vflag[k] = *(const int4*)(ss + 8 * k + 4 * hh);
+
+    // S^T = KV . Q^T  (rows x heads): independent accumulation chains (the
+    // MFMA pipeline would otherwise wait out each result), operands loaded PF
+    // steps ahead
+    constexpr int PF = 3, NCH = 1;
+    v16f sch[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) sch[c] = v16f{};
+    v8bf kring[PF], qring[PF];
+    auto qfrag = [&](int st) -> v8bf { return *(lds_v8bf*)(ql + (st - kQReg) * 1024); };
 #pragma unroll
     for (int st = 0; st < PF; ++st) kring[st] = *(lds_v8bf*)(cur + sbase[st & 3] + 4096 * (st >> 2));
 #pragma unroll
     for (int st = 0; st < 36; ++st) {
       const v8bf kf = kring[st % PF];
-      if (st + PF < 36) kring[st % PF] = *(lds_v8bf*)(cur + sbase[(st + PF) & 3] + 4096 * ((st + PF) >> 2));
-      sacc = mfma_bf16(kf, qb[st], sacc);
+      const v8bf qf = st < kQReg ? qb[st < kQReg ? st : 0] : qring[st % PF];
+      if (st + PF < 36) {
+        kring[st % PF] = *(lds_v8bf*)(cur + sbase[(st + PF) & 3] + 4096 * ((st + PF) >> 2));
+        if (st + PF >= kQReg) qring[st % PF] = qfrag(st + PF);
+      }
+      sch[st % NCH] = mfma_bf16(kf, qf, sch[st % NCH]);
+      // keep each prefetch PF steps ahead of its use (the scheduler would sink it)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    v16f sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = sch[0][r];
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) acc += sch[c][r];
+      sacc[r] = acc;
     }
     // online softmax over the tile's rows (log2 domain); lane owns head nn,
     // rows 8*(r/4) + 4*hh + r%4
@@ -345,8 +430,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-      sv[r] = ss[row] >= 0 ? sacc[r] * a.scale_log2 : -INFINITY;
+      const int4 f = vflag[r >> 2];
+      const int slot = (r & 3) == 0 ? f.x : (r & 3) == 1 ? f.y : (r & 3) == 2 ? f.z : f.w;
+      sv[r] = slot >= 0 ? sacc[r] * a.scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, sv[r]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -358,9 +444,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int v = 0; v < kVT; ++v)
+      for (int v = 0; v < kVT; ++v) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[v][r] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     float psum = 0.f;
     v8bf pb[2];
@@ -388,12 +476,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const v8bf af = vring[k % PF];
       if (k + PF < 2 * kVT) vring[k % PF] = vfrag((k + PF) >> 1, (k + PF) & 1);
       o[vt] = mfma_bf16(af, pb[mf], o[vt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    if constexpr (FP8) {
-      // buffer (i+1) % kBufs was last read two iterations ago, before the barrier above
-      if (i + 1 < ntiles) commit_fp8(i + 1);
+    if constexpr (!FP8) {
+      keep(held_old);
+      keep(held_new);
     }
+    if constexpr (FP8) {
+      // buffer nxt1 was last read two tiles ago, before the barrier above
+      if (i + 1 < ntiles) commit_fp8(nxt1);
+    }
+  };
+  for (int i = 0; i < ntiles; i += 3) {
+    tile_step(i, T0, T1, T2);
+    if (i + 1 < ntiles) tile_step(i + 1, T1, T2, T0);
+    if (i + 2 < ntiles) tile_step(i + 2, T2, T0, T1);
   }
 
   // ---- finish: normalise and write this column half
