@@ -7,183 +7,178 @@
 //      LLMs", section 3.2: Top-K consumes the index scores.
 //
 // Selected set: the first min(K, n) positions under (score desc, position asc),
-// with -0 == +0.  One workgroup per query row.
+// with -0 == +0.  One 1024-thread workgroup per query row.  Scores are mapped to
+// order-preserving 32-bit keys; (key desc, position asc) is the ascending order
+// of the 64-bit composite (~key << 32 | position), which is unique per row.
 //
-//  1. Scores are mapped to order-preserving 32-bit keys (cached in LDS when the
-//     row fits).  The row's key range [kmin, kmax] is found first.
-//  2. Range-adaptive radix select: each pass histograms the keys inside the
-//     current range into <= 2048 equal-width bins (LDS atomics, with a
-//     wave-uniform fast path for runs of equal bins), walks the histogram from
-//     the top to the bin holding the K-th key, and narrows the range to that
-//     bin.  A 32-bit range closes in at most three passes.  The result is the
-//     threshold key T and the number `need` of keys equal to T to keep.
-//  3. One ordered pass (block-wide prefix sums built from wave ballots/scans)
-//     keeps every key > T and the first `need` keys == T in position order,
-//     which is the deterministic tie-break toward lower positions.
-//  4. order 0 sorts the kept (key desc, position asc) pairs with a bitonic
-//     network in LDS; order 1 writes them in ascending position directly.
+// Fast path (keys held in registers when the row fits, else streamed):
+//  1. Block-wide key range [kmin, kmax].  Rows longer than kDirect also take one
+//     key sample per thread and place a lower bound L on the K-th key: the
+//     sample histogram over [kmin, kmax] gives the bin that holds the r-th
+//     largest sample, r sized so that the keys >= L outnumber K with a wide
+//     margin.  Shorter rows use L = kmin.
+//  2. Histogram of the keys >= L (a few thousand LDS atomics instead of one
+//     per key) over 2048 equal-width bins of [L, kmax].  A suffix scan gives
+//     each bin's start in the output order and the bin b* holding the last
+//     selected key.
+//  3. Keys in bins >= b* are scattered into their bins; each one's rank inside
+//     its bin (a short brute-force count over the composite) gives its final
+//     place.  Order 0 writes it there directly; order 1 sets a position bitmap
+//     and compacts it in position order.
+// The fast path is exact whenever it completes.  It hands the row to the exact
+// radix path below when its assumptions fail (fewer than K keys >= L, a bin
+// with more than kMaxBin entries, e.g. long runs of equal scores).
+//
+// Exact path: range-adaptive radix select (<= 2048 bins per pass, three passes
+// close a 32-bit range), an ordered pass that keeps every key above the
+// threshold and the lowest-position ties, and a bitonic sort for order 0.
 #include "sia_common.hpp"
 #include "sia_internal.hpp"
 
 namespace sia {
 
-constexpr int kTopkThreads = 512;
-constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kNT = 1024;
+constexpr int kNW = kNT / 64;
 constexpr int kBins = 2048;
 constexpr int kMaxK = 2048;
-constexpr int kCacheKeys = 32768;
+constexpr int kMaxBin = 256;
+constexpr int kBuf = kMaxK + kMaxBin;
+constexpr int kStreamWords = 8192;  // order-1 bitmap of streamed rows: 262144 positions
+constexpr int kDirect = 4096;
 
-struct TopkShared {
-  uint32_t hist[kBins];
-  uint64_t sel[kMaxK];
-  uint32_t red[2 * kTopkWaves];
-  uint32_t scan[kTopkWaves];
-  uint32_t found_bin;
-  uint32_t found_above;
+// ---- wave / block primitives ------------------------------------------------
+struct OpAdd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct OpMin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct OpMax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
 };
 
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  uint32_t r = red[0];
-  for (int i = 1; i < kTopkWaves; ++i) r = min(r, red[i]);
-  __syncthreads();
-  return r;
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWMASK, 0xf, false);
 }
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  uint32_t r = red[0];
-  for (int i = 1; i < kTopkWaves; ++i) r = max(r, red[i]);
-  __syncthreads();
-  return r;
+// Inclusive scan inside each row of 16 lanes (row_shr 1, 2, 4, 8).
+template <typename Op>
+__device__ __forceinline__ uint32_t row_incl(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp<0x111, 0xf>(id, v));
+  v = op(v, dpp<0x112, 0xf>(id, v));
+  v = op(v, dpp<0x114, 0xf>(id, v));
+  v = op(v, dpp<0x118, 0xf>(id, v));
+  return v;
+}
+// Inclusive scan over the wave in lane order (rows joined with row_bcast 15/31).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl(uint32_t v, uint32_t id, Op op) {
+  v = row_incl(v, id, op);
+  v = op(v, dpp<0x142, 0xa>(id, v));
+  v = op(v, dpp<0x143, 0xc>(id, v));
+  return v;
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_all(uint32_t v, uint32_t id, Op op) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl(v, id, op), 63);
+}
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Combines one value per wave (slot[kNW], written before the last barrier).
+template <typename Op>
+__device__ __forceinline__ uint32_t waves_all(const uint32_t* slot, uint32_t id, Op op) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t x = lane < kNW ? slot[lane] : id;
+  return (uint32_t)__builtin_amdgcn_readlane((int)row_incl(x, id, op), kNW - 1);
 }
 
-// Exclusive prefix sum over the block (thread order); returns the block total in *total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scan, uint32_t* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = (uint32_t)__shfl_up((int)inc, o, 64);
-    if (lane >= o) inc += u;
-  }
-  if (lane == 63) scan[w] = inc;
+// Exclusive prefix sum over the block in thread order, and the block total.
+// One barrier inside; `slot` (kNW words) must not be written again before the
+// next barrier that every thread passes after this call.
+__device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t* slot, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = wave_index();
+  const uint32_t inc = wave_incl(v, 0u, OpAdd{});
+  if (lane == 63) slot[w] = inc;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-  for (int i = 0; i < kTopkWaves; ++i) {
-    const uint32_t x = scan[i];
-    before += (i < w) ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  *total = tot;
+  const uint32_t x = row_incl(lane < kNW ? slot[lane] : 0u, 0u, OpAdd{});
+  const uint32_t before = w ? (uint32_t)__builtin_amdgcn_readlane((int)x, w - 1) : 0u;
+  total = (uint32_t)__builtin_amdgcn_readlane((int)x, kNW - 1);
   return before + inc - v;
 }
 
-template <bool CACHED>
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ scores, int64_t ld, SeqArgs s,
-                                                       int K, int order, int32_t* __restrict__ idx,
-                                                       float* __restrict__ vals) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem_raw);
-  uint32_t* cache = reinterpret_cast<uint32_t*>(smem_raw + sizeof(TopkShared));
+// Shift that maps a key range of `range` values onto at most kBins bins.
+__device__ __forceinline__ int bin_shift(uint64_t range) {
+  const int bits = range > 1 ? 64 - __clzll((long long)(range - 1)) : 0;
+  return bits > 11 ? bits - 11 : 0;
+}
 
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
-  const int pos = clampi(s.q_pos[t], -1, (int)lim - 1);
-  const int n = pos + 1;
-  const float* row = scores + (int64_t)t * ld;
-  int32_t* orow = idx + (int64_t)t * K;
-  float* vrow = vals ? vals + (int64_t)t * K : nullptr;
+__device__ __forceinline__ uint64_t composite(uint32_t key, int pos) {
+  return ((uint64_t)(~key) << 32) | (uint32_t)pos;
+}
 
-  auto key_at = [&](int i) -> uint32_t { return CACHED ? cache[i] : f2key(row[i]); };
+// ---- exact path ----------------------------------------------------------------
+struct ExactSmem {
+  uint32_t hist[kBins];
+  uint64_t sel[kMaxK];
+  uint32_t red[2][kNW];
+  uint32_t scan[2][kNW];
+  uint32_t found_bin, found_above;
+};
 
-  // ---- 1. keys and their range -------------------------------------------
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
+// Writes out[0 .. min(K, n)) for one row, reading the scores from memory.
+__device__ __noinline__ void topk_exact(const float* __restrict__ row, int n, int K, int order,
+                                        int32_t* __restrict__ orow, float* __restrict__ vrow, ExactSmem& sh) {
+  __syncthreads();  // every thread is done with the fast path's shared state
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index();
+  int pp = 0;  // ping-pong between the two scan slots
+
+  // 1. key range
+  uint32_t T = 0u, need = 0u;
   if (n > K) {
-    const int n4 = n & ~3;
-    for (int i = tid * 4; i < n4; i += kTopkThreads * 4) {
-      const float4 f = *reinterpret_cast<const float4*>(row + i);
-      const uint32_t k0 = f2key(f.x), k1 = f2key(f.y), k2 = f2key(f.z), k3 = f2key(f.w);
-      if (CACHED) {
-        cache[i] = k0; cache[i + 1] = k1; cache[i + 2] = k2; cache[i + 3] = k3;
-      }
-      kmin = min(min(kmin, min(k0, k1)), min(k2, k3));
-      kmax = max(max(kmax, max(k0, k1)), max(k2, k3));
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    for (int i = tid; i < n; i += kNT) {
+      const uint32_t k = f2key(row[i]);
+      kmn = min(kmn, k);
+      kmx = max(kmx, k);
     }
-    for (int i = n4 + tid; i < n; i += kTopkThreads) {
-      const uint32_t k0 = f2key(row[i]);
-      if (CACHED) cache[i] = k0;
-      kmin = min(kmin, k0);
-      kmax = max(kmax, k0);
+    kmn = wave_all(kmn, 0xffffffffu, OpMin{});
+    kmx = wave_all(kmx, 0u, OpMax{});
+    if (lane == 0) {
+      sh.red[0][w] = kmn;
+      sh.red[1][w] = kmx;
     }
-    kmin = block_min_u32(kmin, sh.red);
-    kmax = block_max_u32(kmax, sh.red + kTopkWaves);
-  } else if (CACHED) {
-    for (int i = tid; i < n; i += kTopkThreads) cache[i] = f2key(row[i]);
     __syncthreads();
-  }
+    kmn = waves_all(sh.red[0], 0xffffffffu, OpMin{});
+    kmx = waves_all(sh.red[1], 0u, OpMax{});
 
-  // ---- 2. threshold key ----------------------------------------------------
-  uint32_t T = 0u;
-  uint32_t need = 0u;
-  if (n > K) {
-    uint32_t lo = kmin;
-    uint64_t range = (uint64_t)kmax - kmin + 1;
+    // 2. threshold key: narrow [lo, lo + range) to the bin holding the K-th key
+    uint32_t lo = kmn;
+    uint64_t range = (uint64_t)kmx - kmn + 1;
     need = (uint32_t)K;
     while (range > 1) {
-      const int bits = 64 - __clzll((long long)(range - 1));
-      const int shift = bits > 11 ? bits - 11 : 0;
+      const int shift = bin_shift(range);
       const int nb = (int)((range - 1) >> shift) + 1;
-      for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
+      for (int i = tid; i < kBins; i += kNT) sh.hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += kTopkThreads) {
-        const uint32_t k = key_at(i);
-        const bool in = (uint64_t)(k - lo) < range && k >= lo;
-        const uint32_t bin = (k - lo) >> shift;
-        const uint64_t m = __ballot(in);
-        if (m) {
-          const int first = __ffsll((unsigned long long)m) - 1;
-          const uint32_t fb = (uint32_t)__shfl((int)bin, first, 64);
-          const uint64_t same = __ballot(in && bin == fb);
-          if (same == m) {
-            if (lane == first) atomicAdd(&sh.hist[fb], (uint32_t)__popcll(m));
-          } else if (in) {
-            atomicAdd(&sh.hist[bin], 1u);
-          }
-        }
+      for (int i = tid; i < n; i += kNT) {
+        const uint32_t k = f2key(row[i]);
+        if (k >= lo && (uint64_t)(k - lo) < range) atomicAdd(&sh.hist[(k - lo) >> shift], 1u);
       }
       __syncthreads();
-      // thread i owns bins [4i, 4i+4); suffix sums from the top bin down
-      const int b0 = tid * 4;
-      uint32_t c = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c += (b0 + j < nb) ? sh.hist[b0 + j] : 0u;
-      // suffix (exclusive) over threads: count in bins above my range
+      // thread t owns bins hb and hb - 1, counted from the top
+      const int hb = kBins - 1 - 2 * tid;
+      const uint32_t c0 = hb < nb ? sh.hist[hb] : 0u, c1 = hb - 1 < nb ? sh.hist[hb - 1] : 0u;
       uint32_t tot;
-      const uint32_t pre = block_excl_scan(c, sh.scan, &tot);
-      const uint32_t above = tot - pre - c;
-      if (above < need && need <= above + c) {
-        uint32_t acc = above;
-        for (int j = 3; j >= 0; --j) {
-          const int bj = b0 + j;
-          if (bj >= nb) continue;
-          const uint32_t hj = sh.hist[bj];
-          if (acc + hj >= need) {
-            sh.found_bin = (uint32_t)bj;
-            sh.found_above = acc;
-            break;
-          }
-          acc += hj;
-        }
+      const uint32_t a0 = block_excl(c0 + c1, sh.scan[pp], tot);
+      pp ^= 1;
+      const uint32_t a1 = a0 + c0;
+      if (a0 < need && need <= a0 + c0) {
+        sh.found_bin = (uint32_t)hb;
+        sh.found_above = a0;
+      }
+      if (a1 < need && need <= a1 + c1) {
+        sh.found_bin = (uint32_t)(hb - 1);
+        sh.found_above = a1;
       }
       __syncthreads();
       const uint32_t bsel = sh.found_bin, above_sel = sh.found_above;
@@ -198,29 +193,30 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
     T = lo;
   }
 
-  // ---- 3. ordered selection ------------------------------------------------
+  // 3. ordered selection: keys > T, then the lowest positions among keys == T
   uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < n; base += kTopkThreads * 4) {
+  for (int base = 0; base < n; base += kNT * 4) {
     uint32_t kk[4];
-    int cnt_gt = 0, cnt_eq = 0;
+    uint32_t cnt_gt = 0, cnt_eq = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + tid * 4 + j;
-      kk[j] = i < n ? key_at(i) : 0u;
-      cnt_gt += kk[j] > T;
+      kk[j] = i < n ? f2key(row[i]) : 0u;
+      cnt_gt += (i < n) && kk[j] > T;
       cnt_eq += (i < n) && kk[j] == T && need > 0;
     }
     uint32_t tot;
-    const uint32_t pre = block_excl_scan((uint32_t)cnt_gt | ((uint32_t)cnt_eq << 16), sh.scan, &tot);
+    const uint32_t pre = block_excl(cnt_gt | (cnt_eq << 16), sh.scan[pp], tot);
+    pp ^= 1;
     uint32_t g = run_gt + (pre & 0xffffu), e = run_eq + (pre >> 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + tid * 4 + j;
-      const bool gt = kk[j] > T;
+      const bool gt = (i < n) && kk[j] > T;
       const bool eq = (i < n) && kk[j] == T && need > 0;
       if (gt || (eq && e < need)) {
         const uint32_t slot = g + (e < need ? e : need);
-        sh.sel[slot] = ((uint64_t)(~kk[j]) << 32) | (uint32_t)i;
+        sh.sel[slot] = composite(kk[j], i);
       }
       g += gt;
       e += eq;
@@ -230,16 +226,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   }
   __syncthreads();
 
-  // ---- 4. output -------------------------------------------------------------
-  const int cnt = n < K ? (n > 0 ? n : 0) : K;
+  // 4. output
+  const int cnt = n < K ? n : K;
   if (order == 0 && cnt > 1) {
     int P = 1;
     while (P < cnt) P <<= 1;
-    for (int i = cnt + tid; i < P; i += kTopkThreads) sh.sel[i] = ~0ull;
+    for (int i = cnt + tid; i < P; i += kNT) sh.sel[i] = ~0ull;
     __syncthreads();
     for (int k = 2; k <= P; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < P / 2; i += kTopkThreads) {
+        for (int i = tid; i < P / 2; i += kNT) {
           const int a = (i / j) * 2 * j + (i % j);
           const int bb = a + j;
           const uint64_t x = sh.sel[a], y = sh.sel[bb];
@@ -253,32 +249,284 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       }
     }
   }
-  for (int i = tid; i < K; i += kTopkThreads) {
-    if (i < cnt) {
-      const uint64_t v = sh.sel[i];
-      orow[i] = (int32_t)(uint32_t)v;
-      if (vrow) vrow[i] = key2f(~(uint32_t)(v >> 32));
-    } else {
-      orow[i] = -1;
-      if (vrow) vrow[i] = -INFINITY;
+  // order 1 keeps the selection pass's ascending position order
+  for (int i = tid; i < cnt; i += kNT) {
+    const uint64_t v = sh.sel[i];
+    orow[i] = (int32_t)(uint32_t)v;
+    if (vrow) vrow[i] = key2f(~(uint32_t)(v >> 32));
+  }
+}
+
+// ---- fast path -------------------------------------------------------------------
+template <int PER>
+struct FastSmem {
+  static constexpr int kWords = PER > 0 ? kNT * PER / 32 : kStreamWords;
+  uint32_t hs[kBins];     // sample histogram
+  uint32_t hist[kBins];   // histogram of the keys >= L
+  uint32_t above[kBins];  // keys in higher bins = the bin's first output slot
+  uint32_t cur[kBins];    // fill cursors
+  uint64_t buf[kBuf];     // composites of bins >= b*, grouped by bin
+  uint32_t bitmap[kWords];
+  uint32_t red[3][kNW];
+  uint32_t scan[3][kNW];
+  uint32_t maxm[kNW];
+  uint32_t L, bstar, estar;
+};
+template <int PER>
+union TopkSmem {
+  FastSmem<PER> f;
+  ExactSmem x;
+};
+
+// Calls f(key, position) for every position of the row this thread covers;
+// key 0 marks a position past the row's end.  Position of register slot
+// (j, q): (j * kNT + tid) * 4 + q.
+template <int PER, typename F>
+__device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1], const float* __restrict__ row,
+                                         int n, F&& f) {
+  if constexpr (PER > 0) {
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f(key[4 * j + q], (j * kNT + (int)threadIdx.x) * 4 + q);
+  } else {
+    for (int i = (int)threadIdx.x * 4; i < n; i += kNT * 4) {
+      uint32_t k[4];
+      if (i + 4 <= n) {
+        const float4 v = *reinterpret_cast<const float4*>(row + i);
+        k[0] = f2key(v.x);
+        k[1] = f2key(v.y);
+        k[2] = f2key(v.z);
+        k[3] = f2key(v.w);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) k[q] = i + q < n ? f2key(row[i + q]) : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f(k[q], i + q);
     }
   }
+}
+
+// PER keys per thread live in registers (rows up to kNT * PER); PER = 0 streams
+// the row from memory on every pass.
+template <int PER>
+__global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, int64_t ld, SeqArgs s, int K,
+                                              int order, int32_t* __restrict__ idx, float* __restrict__ vals) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  TopkSmem<PER>& smem = *reinterpret_cast<TopkSmem<PER>*>(smem_raw);
+  FastSmem<PER>& sh = smem.f;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_index();
+  const int t = s.T - 1 - (int)blockIdx.x;  // longest rows first when positions grow with t
+  const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
+  const int pos = clampi(s.q_pos[t], -1, (int)lim - 1);
+  const int n = pos + 1;
+  const float* row = scores + (int64_t)t * ld;
+  int32_t* orow = idx + (int64_t)t * K;
+  float* vrow = vals ? vals + (int64_t)t * K : nullptr;
+
+  const int sel = n < K ? n : K;
+  for (int i = (sel > 0 ? sel : 0) + tid; i < K; i += kNT) {
+    orow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+  if (sel <= 0) return;
+  const int words = (n + 31) >> 5;
+  if (order == 1 && words > FastSmem<PER>::kWords) {
+    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    return;
+  }
+
+  for (int i = tid; i < kBins; i += kNT) {
+    sh.hs[i] = 0;
+    sh.hist[i] = 0;
+    sh.cur[i] = 0;
+  }
+  if (order == 1)
+    for (int i = tid; i < words; i += kNT) sh.bitmap[i] = 0;
+
+  // ---- 1. keys, range, sample ----------------------------------------------------
+  uint32_t key[PER > 0 ? PER : 1];
+  if constexpr (PER > 0) {
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const int i = (j * kNT + tid) * 4;
+      if (i + 4 <= n) {
+        const float4 v = *reinterpret_cast<const float4*>(row + i);
+        key[4 * j] = f2key(v.x);
+        key[4 * j + 1] = f2key(v.y);
+        key[4 * j + 2] = f2key(v.z);
+        key[4 * j + 3] = f2key(v.w);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = i + q < n ? f2key(row[i + q]) : 0u;
+      }
+    }
+  } else {
+    key[0] = 0u;
+  }
+  uint32_t kmn = 0xffffffffu, kmx = 0u;
+  for_keys<PER>(key, row, n, [&](uint32_t k, int) {
+    kmn = min(kmn, k ? k : 0xffffffffu);
+    kmx = max(kmx, k);
+  });
+  const bool sampled = n > kDirect;
+  uint32_t smp = 0u;
+  if (sampled) {
+    if constexpr (PER > 0) {
+      const int jn = min(PER / 4, (n + 4 * kNT - 1) / (4 * kNT));
+      const int sidx = (tid % jn) * 4 + ((tid / jn) & 3);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) smp = i == sidx ? key[i] : smp;
+    } else {
+      smp = f2key(row[(int)(((int64_t)tid * n) / kNT)]);
+    }
+  }
+  kmn = wave_all(kmn, 0xffffffffu, OpMin{});
+  kmx = wave_all(kmx, 0u, OpMax{});
+  const uint32_t wns = (uint32_t)__popcll(__ballot(smp != 0u));
+  if (lane == 0) {
+    sh.red[0][w] = kmn;
+    sh.red[1][w] = kmx;
+    sh.red[2][w] = wns;
+  }
+  __syncthreads();
+  const uint32_t kmin = waves_all(sh.red[0], 0xffffffffu, OpMin{});
+  const uint32_t kmax = waves_all(sh.red[1], 0u, OpMax{});
+  const uint32_t nsamp = waves_all(sh.red[2], 0u, OpAdd{});
+  if (kmax < kmin) {  // no finite score in the row
+    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    return;
+  }
+  const int hb = kBins - 1 - 2 * tid;  // this thread's two bins, counted from the top
+
+  // ---- lower bound L from the sample ------------------------------------------------
+  uint32_t L = kmin;
+  if (sampled && nsamp > 0) {
+    const float e = (float)K * (float)nsamp / (float)n;  // expected samples above the K-th key
+    uint32_t r = (uint32_t)ceilf(1.25f * e + 4.0f * sqrtf(e) + 4.0f);
+    r = r < nsamp ? r : nsamp;
+    const int shs = bin_shift((uint64_t)kmax - kmin + 1);
+    if (smp) atomicAdd(&sh.hs[(smp - kmin) >> shs], 1u);
+    __syncthreads();
+    const uint32_t c0 = sh.hs[hb], c1 = sh.hs[hb - 1];
+    uint32_t tot;
+    const uint32_t a0 = block_excl(c0 + c1, sh.scan[0], tot);
+    const uint32_t a1 = a0 + c0;
+    if (a0 < r && r <= a0 + c0) sh.L = kmin + ((uint32_t)hb << shs);
+    if (a1 < r && r <= a1 + c1) sh.L = kmin + ((uint32_t)(hb - 1) << shs);
+    __syncthreads();
+    L = sh.L;
+  }
+
+  // ---- 2. histogram of the keys >= L ---------------------------------------------
+  const int sh2 = bin_shift((uint64_t)kmax - L + 1);
+  for_keys<PER>(key, row, n, [&](uint32_t k, int) {
+    if (k >= L) atomicAdd(&sh.hist[(k - L) >> sh2], 1u);
+  });
+  __syncthreads();
+  const uint32_t usel = (uint32_t)sel;
+  uint32_t cand;
+  {
+    const uint32_t m0 = sh.hist[hb], m1 = sh.hist[hb - 1];
+    const uint32_t a0 = block_excl(m0 + m1, sh.scan[1], cand);
+    const uint32_t a1 = a0 + m0;
+    sh.above[hb] = a0;
+    sh.above[hb - 1] = a1;
+    if (a0 < usel && usel <= a0 + m0) {
+      sh.bstar = (uint32_t)hb;
+      sh.estar = a0 + m0;
+    }
+    if (a1 < usel && usel <= a1 + m1) {
+      sh.bstar = (uint32_t)(hb - 1);
+      sh.estar = a1 + m1;
+    }
+    uint32_t mm = max(a0 < usel ? m0 : 0u, a1 < usel ? m1 : 0u);
+    mm = wave_all(mm, 0u, OpMax{});
+    if (lane == 0) sh.maxm[w] = mm;
+  }
+  __syncthreads();
+  if (cand < usel) {
+    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    return;
+  }
+  const uint32_t bstar = sh.bstar, estar = sh.estar;
+  const uint32_t maxm = waves_all(sh.maxm, 0u, OpMax{});
+  if (estar > (uint32_t)kBuf || maxm > (uint32_t)kMaxBin) {
+    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    return;
+  }
+
+  // ---- 3. scatter bins >= b*, rank inside each bin ---------------------------------
+  for_keys<PER>(key, row, n, [&](uint32_t k, int p) {
+    if (k >= L) {
+      const uint32_t b = (k - L) >> sh2;
+      if (b >= bstar) sh.buf[sh.above[b] + atomicAdd(&sh.cur[b], 1u)] = composite(k, p);
+    }
+  });
+  __syncthreads();
+  for (int i = tid; i < (int)estar; i += kNT) {
+    const uint64_t v = sh.buf[i];
+    const uint32_t k = ~(uint32_t)(v >> 32);
+    const uint32_t b = (k - L) >> sh2;
+    const uint32_t st = sh.above[b], m = sh.hist[b];
+    uint32_t rank = 0;
+    for (uint32_t j = st; j < st + m; ++j) rank += sh.buf[j] < v;
+    const uint32_t fin = st + rank;
+    if (fin < usel) {
+      const int p = (int)(uint32_t)v;
+      if (order == 0) {
+        orow[fin] = p;
+        if (vrow) vrow[fin] = key2f(k);
+      } else {
+        atomicOr(&sh.bitmap[p >> 5], 1u << (p & 31));
+      }
+    }
+  }
+  if (order == 0) return;
+
+  // order 1: compact the bitmap in position order
+  __syncthreads();
+  const int wpt = (words + kNT - 1) / kNT;
+  const int w0 = tid * wpt;
+  uint32_t c = 0;
+  for (int i = 0; i < wpt; ++i)
+    if (w0 + i < words) c += __popc(sh.bitmap[w0 + i]);
+  uint32_t tot;
+  uint32_t off = block_excl(c, sh.scan[2], tot);
+  for (int i = 0; i < wpt; ++i) {
+    if (w0 + i >= words) break;
+    uint32_t bits = sh.bitmap[w0 + i];
+    while (bits) {
+      const int bpos = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int p = (w0 + i) * 32 + bpos;
+      orow[off] = p;
+      if (vrow) vrow[off] = key2f(f2key(row[p]));
+      ++off;
+    }
+  }
+}
+
+template <int PER>
+static hipError_t launch_rows(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
+                              float* vals, hipStream_t st) {
+  const size_t shm = sizeof(TopkSmem<PER>);
+  hipError_t e = hipFuncSetAttribute((const void*)k_topk<PER>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_topk<PER>, dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
                        float* vals, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
-  if (lim <= kCacheKeys) {
-    const size_t shm = sizeof(TopkShared) + (size_t)kCacheKeys * 4;
-    hipError_t e = hipFuncSetAttribute((const void*)k_topk<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_topk<true>, dim3(s.T), dim3(kTopkThreads), shm, st, scores, ld, s, K, order, idx, vals);
-  } else {
-    hipLaunchKernelGGL(k_topk<false>, dim3(s.T), dim3(kTopkThreads), sizeof(TopkShared), st, scores, ld, s, K,
-                       order, idx, vals);
-  }
-  return hipGetLastError();
+  if (lim <= kNT * 8) return launch_rows<8>(scores, ld, s, K, order, idx, vals, st);
+  if (lim <= kNT * 32) return launch_rows<32>(scores, ld, s, K, order, idx, vals, st);
+  if (lim <= kNT * 64) return launch_rows<64>(scores, ld, s, K, order, idx, vals, st);
+  return launch_rows<0>(scores, ld, s, K, order, idx, vals, st);
 }
 
 }  // namespace sia
