@@ -488,11 +488,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       if (i + 1 < ntiles) commit_fp8(nxt1);
     }
   };
-  for (int i = 0; i < ntiles; i += 3) {
+  // Whole triples in the loop and the remainder after it: a loop body with
+  // conditionally skipped steps merges differently ordered in-flight loads at
+  // its head, and the compiler then drains every load before reading a tile.
+  int i = 0;
+  for (; i + 3 <= ntiles; i += 3) {
     tile_step(i, T0, T1, T2);
-    if (i + 1 < ntiles) tile_step(i + 1, T1, T2, T0);
-    if (i + 2 < ntiles) tile_step(i + 2, T2, T0, T1);
+    tile_step(i + 1, T1, T2, T0);
+    tile_step(i + 2, T2, T0, T1);
   }
+  if (i < ntiles) tile_step(i, T0, T1, T2);
+  if (i + 1 < ntiles) tile_step(i + 1, T1, T2, T0);
 
   // ---- finish: normalise and write this column half
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
