@@ -24,8 +24,9 @@
 //     (the row order inside the MFMA K dimension is chosen to match it) and V^T
 //     is read with ds_read_b64_tr_b16 transposing loads.
 // The LDS tile is row-major (72 16-byte chunks per row) with the chunk index
-// XOR-swizzled by f(row) = 2*(row%4) + (row/4)%2, which keeps both the 128-bit
-// row reads and the transposing reads free of bank conflicts.
+// XOR-swizzled by a 3-bit function of row bits 1..3 (see swz), which keeps both
+// the 128-bit row reads and the transposing reads free of bank conflicts on
+// gfx950's 64 four-byte LDS banks.
 //
 // Decode splits a token's rows over several workgroups; each writes a partial
 // (O normalised over its rows, LSE) and a combine kernel merges them with
@@ -126,7 +127,15 @@ constexpr int kChunks = kD / 8;                   // 72 chunks of 8 bf16 (16 byt
 constexpr int kRowsTile = 32;
 constexpr int kTileBytes = kRowsTile * kD * 2;   // 36864
 
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// Chunk swizzle of a tile row: bit 1 of the row -> bit 2, bit 3 -> bit 1, bit 2
+// -> bit 0.  A 128-bit read of one chunk per row by 16 consecutive lanes (rows
+// r..r+15) then covers all 64 banks once: even rows and odd rows each take all
+// eight swizzle values.  A transposing read covers rows r..r+3 (r % 4 == 0),
+// where rows two apart differ in swizzle bit 2 and so land in disjoint banks.
+// Rows 16 apart share the swizzle.
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) & 1) << 2) | (((row >> 3) & 1) << 1) | ((row >> 2) & 1);
+}
 
 __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -169,20 +178,6 @@ constexpr int kVT = kVH / 32;  // 32-column output tiles per half
 // expcnt = 7 (no wait), lgkmcnt = 0
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
 template <int N> __device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N)); }
-// Nine 16-byte direct loads of one row group (chunk groups m = 0..8 of 8 rows):
-// global src + 128*m -> LDS dst + 4096*m, all from one address register pair.
-template <int M>
-__device__ __forceinline__ void dma_row(const unsigned char* src, lds_u8* dst) {
-  if constexpr (M < 9) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 4096 * M - 128 * M), 16, 128 * M, 0);
-    dma_row<M + 1>(src, dst);
-  }
-}
-// Keeps a value's registers allocated up to this point (emits no instruction).
-__device__ __forceinline__ void keep_live(const void* p) { asm volatile("" ::"v"(p)); }
-
-// direct global->LDS loads each lane issues per bf16 tile
-template <int NW> constexpr int kBf16LoadsPerTile() { return 9 * ((4 + NW - 1) / NW); }
 
 template <int NW, bool FP8>
 __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
@@ -233,33 +228,32 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
 
   // ---- gather: bf16 rows go global -> LDS directly --------------------------
   // wave instruction (row group rg, chunk group m) covers rows 8rg..8rg+7 and
-  // chunks 8m..8m+7; lane L: row 8rg + L/8, chunk 8m + ((L%8) ^ swz(row)).
+  // chunks 8m..8m+7; lane L: row 8rg + L/8, chunk 8m + ((L%8) ^ swz(row)), so
+  // that one 16-byte LDS write per lane fills 64 consecutive slots (1 KB).
+  // The rows pass through registers: the next tile is loaded while this one is
+  // computed and written to LDS after it.  (Direct global->LDS loads would keep
+  // a load that may touch LDS in flight during the whole tile, and the compiler
+  // then waits for every outstanding LDS read at each operand use.)
   const int g_sub = lane & 7;
-  // All nine loads of a row group share one address register pair: chunk group m
-  // is reached through the instruction offset 128*m, which the hardware adds to
-  // both the global and the LDS address, so the LDS base is pre-compensated.  The
-  // pair is returned so that the caller keeps it allocated while the loads are in
-  // flight (a load into LDS counts as a store whose address is read late; reusing
-  // the registers would make the compiler drain every outstanding load).
   constexpr int kRG = (4 + NW - 1) / NW;   // 8-row groups per wave
-  struct Held { const unsigned char* p[kRG]; };
-  auto issue_bf16 = [&](int i, lds_u8* dst) __attribute__((always_inline)) -> Held {
+  v4i bstage[FP8 ? 1 : kRG * 9];
+  auto issue_bf16 = [&](int i) __attribute__((always_inline)) {
     const int32_t* ss = sslot + i * kRowsTile;
-    Held h;
 #pragma unroll
     for (int k = 0; k < kRG; ++k) {
-      const int rg = wave + NW * k;
-      const int r = 8 * rg + (lane >> 3);
+      const int r = 8 * (wave + NW * k) + (lane >> 3);
       const int slot = ss[r] >= 0 ? ss[r] : 0;
       const unsigned char* src = kvb + (int64_t)slot * (kD * 2) + 16 * (g_sub ^ swz(r));
-      h.p[k] = src;
-      dma_row<0>(src, dst + 64 * rg * 16);
-    }
-    return h;
-  };
-  auto keep = [&](const Held& h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < kRG; ++k) keep_live(h.p[k]);
+      for (int m = 0; m < 9; ++m) bstage[k * 9 + m] = *(const v4i*)(src + 128 * m);
+    }
+  };
+  auto commit_bf16 = [&](lds_u8* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kRG; ++k)
+#pragma unroll
+      for (int m = 0; m < 9; ++m)
+        *(lds_v4i*)(dst + 4096 * m + 1024 * (wave + NW * k) + 16 * lane) = bstage[k * 9 + m];
   };
 
   // ---- gather: fp8 rows go through registers and are dequantized to bf16 ----
@@ -333,58 +327,49 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   //  offset jrow = s'/4 and vcol quad qd = s'%4; lane group g = lane/16.
   const int g = lane >> 4, sp = lane & 15, jrow = sp >> 2, qd = sp & 3;
   const int vrow0 = 4 * (g >> 1) + jrow;            // + 8a + 16mf
-  const int vsw = swz(vrow0);                       // same for every a, mf
-  int vbase[2];
+  // one base per (column parity, a); the swizzle is the same for mf = 0, 1
+  int vbase[2][2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
-    vbase[par] = 128 * vrow0 + 16 * ((4 * par + 2 * (g & 1) + (qd >> 1)) ^ vsw) + 8 * (qd & 1) +
-                 4096 * 4 * vhalf;   // column half: chunk groups 4..7
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) {
+      const int vr = vrow0 + 8 * aa;
+      vbase[par][aa] = 128 * vr + 16 * ((4 * par + 2 * (g & 1) + (qd >> 1)) ^ swz(vr)) + 8 * (qd & 1) +
+                       4096 * 4 * vhalf;   // column half: chunk groups 4..7
+    }
 
   v16f o[kVT];
 #pragma unroll
   for (int v = 0; v < kVT; ++v) o[v] = v16f{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  Held held_old{}, held_new{};   // address pairs of the two tiles whose loads may be in flight
   lds_u8* const T0 = (lds_u8*)tile0;
   lds_u8* const T1 = (lds_u8*)tile1;
   lds_u8* const T2 = (lds_u8*)tile2;
-  // prologue: tile 0 (and tile 1 for bf16) in flight
+  // prologue: tile 0 staged and written
   __syncthreads();
   if (ntiles > 0) {
     if constexpr (FP8) {
       issue_fp8(0);
       commit_fp8(T0);
     } else {
-      held_old = issue_bf16(0, T0);
-      held_new = issue_bf16(1, T1);   // unconditional, like the in-loop issues
+      issue_bf16(0);
+      commit_bf16(T0);
     }
   }
 
-  // one tile: compute on `cur`; the loads of tile i+1 (fp8: committed into
-  // `nxt1`) or tile i+2 (bf16: straight into `nxt2`) overlap with it
+  // one tile: compute on `cur` while tile i+1 is loaded into registers, then
+  // write it into `nxt1` (last read two tiles ago, before this tile's barrier)
   auto tile_step = [&](int i, lds_u8* cur, lds_u8* nxt1, lds_u8* nxt2) __attribute__((always_inline)) {
-    // Tile i has landed once at most one later tile's direct loads are still in
-    // flight (bf16), and every wave's LDS writes are done.  A plain s_barrier is
-    // used on purpose: __syncthreads() would also drain the loads of tile i+1.
-    // (the wait is a compiler-visible builtin so that its own bookkeeping of the
-    // in-flight direct loads stays exact)
-    // With the loads issued unconditionally, exactly one younger tile is always in flight.
-    if constexpr (!FP8) {
-      keep(held_old);
-      keep(held_new);
-      wait_vm_lgkm0<kBf16LoadsPerTile<NW>()>();
-    } else {
-      wait_vm_lgkm0<63>();
-    }
+    // every wave's LDS writes of tile i are done (lgkmcnt 0) before the barrier;
+    // the loads of tile i+1 are issued after it
+    wait_vm_lgkm0<63>();
     asm volatile("s_barrier" ::: "memory");
-    if constexpr (FP8) {
-      if (i + 1 < ntiles) issue_fp8(i + 1);
-    } else {
-      // unconditional (past the end it re-reads row 0 into a finished buffer), so
-      // the compiler keeps the load's LDS target known and does not drain it
-      held_old = held_new;          // tile i's loads have landed: its pair is free
-      held_new = issue_bf16(i + 2, nxt2);
+    if (i + 1 < ntiles) {
+      if constexpr (FP8)
+        issue_fp8(i + 1);
+      else
+        issue_bf16(i + 1);
     }
     const int32_t* ss = sslot + i * kRowsTile;
 
@@ -463,8 +448,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     // O^T += V^T . P^T ; MFMA mf covers tile rows 16mf + R(hh, jj); operands one step ahead
     auto vfrag = [&](int vt, int mf) -> v8bf {
       const int imm = 4096 * (vt >> 1) + 2048 * mf;
-      const v4bf x0 = lds_tr16(cur, vbase[vt & 1] + imm);
-      const v4bf x1 = lds_tr16(cur, vbase[vt & 1] + imm + 1024);
+      const v4bf x0 = lds_tr16(cur, vbase[vt & 1][0] + imm);
+      const v4bf x1 = lds_tr16(cur, vbase[vt & 1][1] + imm);
       return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     v8bf vring[PF];
@@ -479,13 +464,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if constexpr (!FP8) {
-      keep(held_old);
-      keep(held_new);
-    }
-    if constexpr (FP8) {
-      // buffer nxt1 was last read two tiles ago, before the barrier above
-      if (i + 1 < ntiles) commit_fp8(nxt1);
+    if (i + 1 < ntiles) {
+      if constexpr (FP8)
+        commit_fp8(nxt1);
+      else
+        commit_bf16(nxt1);
     }
   };
   // Whole triples in the loop and the remainder after it: a loop body with
