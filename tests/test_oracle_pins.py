@@ -4,6 +4,7 @@ other than itself (library routines, closed forms, brute force, invariants).
 These tests run on the CPU only.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -27,9 +28,18 @@ def test_e4m3_all_codes_vs_torch():
 
 
 def test_e4m3_landmarks():
-    v = O.decode_e4m3(np.array([0x7E, 0x38, 0x08, 0x01, 0x80, 0xB8], dtype=np.uint8))
-    assert v[0] == 448.0 and v[1] == 1.0 and v[2] == 2.0 ** -6 and v[3] == 2.0 ** -9
-    assert v[4] == 0.0 and np.signbit(v[4]) and v[5] == -1.0
+    """Format landmarks from tests/golden/e4m3_landmarks.txt (largest finite,
+    one, smallest normal and subnormal, signed zeros, NaN)."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "e4m3_landmarks.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    codes = np.array([int(c, 16) for c, _ in rows], dtype=np.uint8)
+    got = O.decode_e4m3(codes)
+    for (c, want), g in zip(rows, got):
+        if want == "nan":
+            assert np.isnan(g), c
+        else:
+            w = float(want)
+            assert g == w and np.signbit(g) == want.startswith("-"), (c, g, want)
 
 
 def test_bf16_vs_torch():
