@@ -132,8 +132,8 @@ enum { SIA_OP_TOPK = 0, SIA_OP_MLA_DECODE = 1, SIA_OP_MLA_PREFILL = 2, SIA_OP_IN
  * P2, section 3.1; P3, section 3.1].
  *   scores[t * ld + s] = sum_h w[t,h] * ReLU(qs[t,h] * ks[s] * <q[t,h], k[s]>)
  * for s = 0..q_pos[t] (fp32 accumulate).  Entries s > q_pos[t] are not part of
- * the result; the kernel may write -inf into them up to the next multiple of 64
- * below ld and leaves the rest untouched.
+ * the result: entries q_pos[t] < s < max_visible may be overwritten with -inf,
+ * entries s >= max_visible are never written.
  *   scores  [T, ld] float, 16-byte aligned; ld % 4 == 0, ld >= max_visible.     */
 int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* scores,
                      int64_t ld, hipStream_t stream);
