@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsia.so")
 SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "sia_api.cpp"]
 # per-source extra flags (none needed at present)
-SOURCE_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {}
 
 
 def hipcc() -> str:

@@ -107,6 +107,29 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
     c_end = c_end < c_vis ? c_end : c_vis;
     if (c_begin >= c_end) continue;
 
+    const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
+    float* srow = a.scores + (int64_t)t * a.ld;
+
+    // key pages go through a ring of three register buffers: while page c is
+    // computed, pages c+1 and c+2 are in flight
+    auto load_page = [&](int c, v8i (&kb)[2][2], float& ks) __attribute__((always_inline)) {
+      int page = table[c];
+      page = page < 0 ? 0 : (page >= a.s.num_pages ? a.s.num_pages - 1 : page);
+      const uint8_t* pb = kpool + (int64_t)page * (kPage * 128) + 64 * hh;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint8_t* kr = pb + (32 * kt + nn) * 128;
+        kb[kt][0] = *(const v8i*)(kr);
+        kb[kt][1] = *(const v8i*)(kr + 32);
+      }
+      ks = a.k_scale[(int64_t)page * kPage + lane];
+    };
+    v8i k0[2][2], k1[2][2], k2[2][2];
+    float ks0 = 0.f, ks1 = 0.f, ks2 = 0.f;
+    load_page(c_begin, k0, ks0);
+    if (c_begin + 1 < c_end) load_page(c_begin + 1, k1, ks1);
+    if (c_begin + 2 < c_end) load_page(c_begin + 2, k2, ks2);
+
     // query operand (A): head m = 32*mt + nn
     v8i qa[MT][2];
     float wr[MT][16];
@@ -122,27 +145,8 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
         wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
       }
     }
-    const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
-    float* srow = a.scores + (int64_t)t * a.ld;
-
-    auto load_page = [&](int c, v8i (&kb)[2][2], float& ks) {
-      int page = table[c];
-      page = page < 0 ? 0 : (page >= a.s.num_pages ? a.s.num_pages - 1 : page);
-      const uint8_t* pb = kpool + (int64_t)page * (kPage * 128) + 64 * hh;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint8_t* kr = pb + (32 * kt + nn) * 128;
-        kb[kt][0] = *(const v8i*)(kr);
-        kb[kt][1] = *(const v8i*)(kr + 32);
-      }
-      ks = a.k_scale[(int64_t)page * kPage + lane];
-    };
-
-    v8i kb[2][2], kn[2][2];
-    float ks, ksn;
-    load_page(c_begin, kb, ks);
-    for (int c = c_begin; c < c_end; ++c) {
-      if (c + 1 < c_end) load_page(c + 1, kn, ksn);
+    // scores of page c from buffer kb, then buffer kb takes page c+3
+    auto step = [&](int c, v8i (&kb)[2][2], float& ks) __attribute__((always_inline)) {
       float p[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -164,15 +168,16 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
       const int s = c * 64 + lane;
       if (s > pos) score = -INFINITY;
       if (s < a.s.max_visible) srow[s] = score;
-      if (c + 1 < c_end) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          kb[kt][0] = kn[kt][0];
-          kb[kt][1] = kn[kt][1];
-        }
-        ks = ksn;
-      }
+      if (c + 3 < c_end) load_page(c + 3, kb, ks);
+    };
+    int c = c_begin;
+    for (; c + 3 <= c_end; c += 3) {
+      step(c, k0, ks0);
+      step(c + 1, k1, ks1);
+      step(c + 2, k2, ks2);
     }
+    if (c < c_end) step(c, k0, ks0);
+    if (c + 1 < c_end) step(c + 1, k1, ks1);
   }
 }
 
@@ -190,7 +195,7 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
   // enough waves to keep every CU busy: split the key range of each query
   // block when there are few query blocks (decode), keep it whole otherwise
   const int cus = num_cus();
-  const int64_t target_items = (int64_t)cus * 2 * 2;
+  const int64_t target_items = (int64_t)cus * 2;
   int n_ranges = (int)((target_items + n_qblocks - 1) / n_qblocks);
   n_ranges = n_ranges < 1 ? 1 : (n_ranges > n_chunks ? n_chunks : n_ranges);
   const int cpi = (n_chunks + n_ranges - 1) / n_ranges;

@@ -19,7 +19,8 @@
 //   * S^T[row, head] = KV_tile . Q^T on v_mfma_f32_32x32x16_bf16: the KV tile is
 //     the LDS operand, the wave's 32 query heads stay in registers for the
 //     whole token;
-//   * online softmax per head is lane-local (each lane owns one head column);
+//   * softmax per head is lane-local (each lane owns one head column) against a
+//     fixed per-head reference, so the accumulator is never rescaled;
 //   * O^T[vcol, head] += V^T . P^T: P^T comes straight from the S^T accumulator
 //     (the row order inside the MFMA K dimension is chosen to match it) and V^T
 //     is read with ds_read_b64_tr_b16 transposing loads.
@@ -338,16 +339,27 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
                        4096 * 4 * vhalf;   // column half: chunk groups 4..7
     }
 
+  // Softmax reference: p = 2^(l - m_ref) with one fixed m_ref per head, the
+  // largest logit of the first tile that has a valid row, so no tile rescales
+  // the accumulator.  m_ref never exceeds the true maximum, so nothing that
+  // matters underflows; if a later tile's logits exceed m_ref by more than
+  // 2^100 (which could overflow the fp32 sums), the workgroup runs its rows
+  // once more with m_ref = the maximum seen over all of them.
   v16f o[kVT];
-#pragma unroll
-  for (int v = 0; v < kVT; ++v) o[v] = v16f{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+  bool overflow = false;
 
   lds_u8* const T0 = (lds_u8*)tile0;
   lds_u8* const T1 = (lds_u8*)tile1;
   lds_u8* const T2 = (lds_u8*)tile2;
-  // prologue: tile 0 staged and written
   __syncthreads();
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+  for (int v = 0; v < kVT; ++v) o[v] = v16f{};
+  l_run = 0.f;
+  overflow = false;
+  if (pass == 1) m_ref = m_seen;
+  // prologue: tile 0 staged and written
   if (ntiles > 0) {
     if constexpr (FP8) {
       issue_fp8(0);
@@ -421,25 +433,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       tmax = fmaxf(tmax, sv[r]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // lazy rescale: move the running max only when it grows by more than 2^8
-    const bool grow = tmax > m_run + 8.f;
-    if (__ballot(grow)) {
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int v = 0; v < kVT; ++v) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[v][r] *= alpha;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    m_seen = fmaxf(m_seen, tmax);
+    if (m_ref == -INFINITY) m_ref = tmax;
+    overflow |= tmax > m_ref + 100.f;
     float psum = 0.f;
     v8bf pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pv = (m_run == -INFINITY) ? 0.f : fast_exp2(sv[r] - m_run);
+      const float pv = (m_ref == -INFINITY) ? 0.f : fast_exp2(sv[r] - m_ref);
       psum += pv;
       pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
     }
@@ -482,11 +483,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   }
   if (i < ntiles) tile_step(i, T0, T1, T2);
   if (i + 1 < ntiles) tile_step(i + 1, T1, T2, T0);
+  // every wave agrees on a second pass; the barrier also retires this pass's tiles
+  if (!__syncthreads_or(overflow)) break;
+  }
 
   // ---- finish: normalise and write this column half
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  const float lse_v = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   const int vc0 = kVH * vhalf;
   if (a.splits == 1) {
     uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + head) * kDc + vc0;

@@ -253,3 +253,38 @@ def test_split_count_invariance():
     b = sia.sparse_mla_prefill(q, kv, seq, idx, K, wl.softmax_scale).float()
     torch.cuda.synchronize()
     assert torch.allclose(a, b, atol=1e-2, rtol=1e-2)
+
+
+@pytest.mark.parametrize("name", ["decode_tiny", "prefill_tiny"])
+def test_sparse_mla_wide_logit_range(name):
+    """Logits spread over hundreds of units (softmax scale 6): later tiles
+    exceed the first tile's maximum by far more than 2^100, which takes the
+    kernels' second pass with the overall maximum as the softmax reference.
+    (bf16 caches only: the fp8 path rounds dequantized latent values to bf16,
+    an error that logits of this size amplify beyond the attention tolerance.)"""
+    wl = workload(name)
+    print(f"[mla-wide-logits] {name}", flush=True)
+    K, H = wl.cfg["K"], wl.cfg["H"]
+    scale = 6.0
+    _, sel, _ = oracle_run(name)
+    att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), sel, scale)
+    # the one-split entry sees the listed rows in order: check that some token's
+    # later rows really exceed its first 32 rows' maximum by > 100 (log2 units)
+    kvd, seqd = wl.oracle_kv(), wl.oracle_seq()
+    triggered = 0
+    for t in range(wl.Tq):
+        ids = sel[t][sel[t] >= 0]
+        if len(ids) <= 32:
+            continue
+        rows = O.kv_rows(kvd, O.physical_slots(seqd["block_table"][int(seqd["q_seq"][t])], ids, 64))
+        qd = O.decode_bf16(wl.q[t]) if wl.q.dtype == np.uint16 else wl.q[t].astype(np.float64)
+        lg = (qd @ rows.T) * scale / np.log(2.0)
+        triggered += int(np.any(lg[:, 32:].max(axis=1) > lg[:, :32].max(axis=1) + 100.0))
+    assert triggered > 0
+    seq, _, q, kv = upload(wl)
+    idx = dev(np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32))
+    lse = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        out = fn(q, kv, seq, idx, K, scale, lse=lse)
+        torch.cuda.synchronize()
+        check_attention(kind_of(wl), to_np_out(out), lse.cpu().numpy(), att, range(wl.Tq))
