@@ -249,6 +249,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       for (int m = 0; m < 9; ++m) bstage[k * 9 + m] = *(const v4i*)(src + 128 * m);
     }
   };
+  // the same loads one at a time (q = 9k + m), for interleaving with MFMAs
+  auto bf16_src = [&](int i, int k) __attribute__((always_inline)) -> const unsigned char* {
+    const int r = 8 * (wave + NW * k) + (lane >> 3);
+    const int slot = sslot[i * kRowsTile + r];
+    return kvb + (int64_t)(slot >= 0 ? slot : 0) * (kD * 2) + 16 * (g_sub ^ swz(r));
+  };
+  auto commit_bf16_one = [&](lds_u8* dst, int q) __attribute__((always_inline)) {
+    *(lds_v4i*)(dst + 4096 * (q % 9) + 1024 * (wave + NW * (q / 9)) + 16 * lane) = bstage[q];
+  };
   auto commit_bf16 = [&](lds_u8* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kRG; ++k)
@@ -375,13 +384,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   auto tile_step = [&](int i, lds_u8* cur, lds_u8* nxt1, lds_u8* nxt2) __attribute__((always_inline)) {
     // every wave's LDS writes of tile i are done (lgkmcnt 0) before the barrier;
     // the loads of tile i+1 are issued after it
+    const bool has_next = i + 1 < ntiles;
+    // bf16: source rows of tile i+1 (slot table reads, before the barrier)
+    const unsigned char* nsrc[FP8 ? 1 : kRG];
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int k = 0; k < kRG; ++k) nsrc[k] = bf16_src(has_next ? i + 1 : i, k);
+    }
     wait_vm_lgkm0<63>();
     asm volatile("s_barrier" ::: "memory");
-    if (i + 1 < ntiles) {
-      if constexpr (FP8)
-        issue_fp8(i + 1);
-      else
-        issue_bf16(i + 1);
+    if constexpr (FP8) {
+      if (has_next) issue_fp8(i + 1);
     }
     const int32_t* ss = sslot + i * kRowsTile;
 
@@ -410,6 +423,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         if (st + PF >= kQReg) qring[st % PF] = qfrag(st + PF);
       }
       sch[st % NCH] = mfma_bf16(kf, qf, sch[st % NCH]);
+      // one row load of tile i+1 per step, in the shadow of the MFMAs
+      if constexpr (!FP8) {
+        if (st < kRG * 9 && has_next) bstage[st] = *(const v4i*)(nsrc[st / 9] + 128 * (st % 9));
+      }
       // keep each prefetch PF steps ahead of its use (the scheduler would sink it)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -438,13 +455,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     overflow |= tmax > m_ref + 100.f;
     float psum = 0.f;
     v8bf pb[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    auto pexp = [&](int r) __attribute__((always_inline)) {
       const float pv = (m_ref == -INFINITY) ? 0.f : fast_exp2(sv[r] - m_ref);
       psum += pv;
       pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
-    }
-    l_run += psum;
+    };
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pexp(r);
 
     // O^T += V^T . P^T ; MFMA mf covers tile rows 16mf + R(hh, jj); operands one step ahead
     auto vfrag = [&](int vt, int mf) -> v8bf {
@@ -453,23 +470,32 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const v4bf x1 = lds_tr16(cur, vbase[vt & 1][1] + imm);
       return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
+    // step k: column tile k % kVT, row half k / kVT (P rows 8..15 are computed
+    // during the first half); one LDS write of tile i+1 per step
     v8bf vring[PF];
 #pragma unroll
-    for (int k = 0; k < PF; ++k) vring[k] = vfrag(k >> 1, k & 1);
+    for (int k = 0; k < PF; ++k) vring[k] = vfrag(k % kVT, k / kVT);
 #pragma unroll
     for (int k = 0; k < 2 * kVT; ++k) {
-      const int vt = k >> 1, mf = k & 1;
+      const int vt = k % kVT, mf = k / kVT;
       const v8bf af = vring[k % PF];
-      if (k + PF < 2 * kVT) vring[k % PF] = vfrag((k + PF) >> 1, (k + PF) & 1);
+      if (k + PF < 2 * kVT) vring[k % PF] = vfrag((k + PF) % kVT, (k + PF) / kVT);
       o[vt] = mfma_bf16(af, pb[mf], o[vt]);
+      if (k < 8) pexp(8 + k);
+      if constexpr (!FP8) {
+        if (k < kRG * 9 && has_next) commit_bf16_one(nxt1, k);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += psum;
 
-    if (i + 1 < ntiles) {
-      if constexpr (FP8)
+    if (has_next) {
+      if constexpr (FP8) {
         commit_fp8(nxt1);
-      else
-        commit_bf16(nxt1);
+      } else {
+#pragma unroll
+        for (int q = 2 * kVT; q < kRG * 9; ++q) commit_bf16_one(nxt1, q);
+      }
     }
   };
   // Whole triples in the loop and the remainder after it: a loop body with
