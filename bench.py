@@ -202,26 +202,42 @@ def main():
         mws = torch.empty(max(nmla, 1), dtype=torch.uint8, device="cuda")
         mla_fn = sia.sparse_mla_decode if sia.workspace_size(sia.OP_MLA_DECODE, sets[0]["seq"], K, H, c["Dc"]) > 0 \
             else sia.sparse_mla_prefill
-        names = ["index_scores", "topk", "sparse_mla"]
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        for i in range(args.warmup + args.steps):
-            s = sets[i % copies]
-            rec = ev[i - args.warmup] if i >= args.warmup else None
-            if rec:
-                rec[0].record(stream)
-            sia.index_scores(s["ix"], s["seq"], scores[i % copies], stream=stream)
-            if rec:
-                rec[1].record(stream)
-            sia.topk(scores[i % copies], s["seq"], K, order=args.order, idx=s["idx"], stream=stream)
-            if rec:
-                rec[2].record(stream)
-            mla_fn(s["q"], s["kv"], s["seq"], s["idx"], K, wl.softmax_scale, out=s["out"], ws=mws, stream=stream)
-            if rec:
-                rec[3].record(stream)
-        torch.cuda.synchronize()
-        for k, nm in enumerate(names):
-            us = 1e3 * sum(r[k].elapsed_time(r[k + 1]) for r in ev) / args.steps
-            breakdown[nm] = round(us, 2)
+        tws = [torch.empty(max(sia.workspace_size(sia.OP_INDEX_TOPK, st["seq"], K, 1, 1), 1), dtype=torch.uint8,
+                           device="cuda") for st in sets]
+
+        def timed(calls):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+            for i in range(args.warmup + args.steps):
+                rec = ev[i - args.warmup] if i >= args.warmup else None
+                for k, (_, fn) in enumerate(calls):
+                    if rec:
+                        rec[k].record(stream)
+                    fn(i)
+                if rec:
+                    rec[-1].record(stream)
+            torch.cuda.synchronize()
+            for k, (nm, _) in enumerate(calls):
+                breakdown[nm] = round(1e3 * sum(r[k].elapsed_time(r[k + 1]) for r in ev) / args.steps, 2)
+
+        def sel(i):   # steps 1 + 2 as the fused call runs them (method chosen by the library)
+            st = sets[i % copies]
+            sia.index_topk(st["ix"], st["seq"], K, order=args.order, idx=st["idx"], ws=tws[i % copies], stream=stream)
+
+        def mla(i):
+            st = sets[i % copies]
+            mla_fn(st["q"], st["kv"], st["seq"], st["idx"], K, wl.softmax_scale, out=st["out"], ws=mws, stream=stream)
+
+        def scr(i):   # the indexer kernel alone, then Top-K over its score matrix
+            st = sets[i % copies]
+            sia.index_scores(st["ix"], st["seq"], scores[i % copies], stream=stream)
+
+        def tk(i):
+            st = sets[i % copies]
+            sia.topk(scores[i % copies], st["seq"], K, order=args.order, idx=st["idx"], stream=stream)
+
+        timed([("index_topk", sel), ("sparse_mla", mla)])
+        timed([("index_scores", scr), ("topk", tk)])
+        breakdown["index_topk_method"] = sia.index_topk_method(sets[0]["ix"], sets[0]["seq"])
         del scores
 
     roofline = None

@@ -126,7 +126,8 @@ typedef struct {
 } sia_kv_in;
 
 /* Operation codes for sia_workspace_size. */
-enum { SIA_OP_TOPK = 0, SIA_OP_MLA_DECODE = 1, SIA_OP_MLA_PREFILL = 2, SIA_OP_INDEX_SELECT_ATTEND = 3 };
+enum { SIA_OP_TOPK = 0, SIA_OP_MLA_DECODE = 1, SIA_OP_MLA_PREFILL = 2, SIA_OP_INDEX_SELECT_ATTEND = 3,
+       SIA_OP_INDEX_TOPK = 4 };
 
 /* Step 1 — indexer scores [P1, "Sparse Attention Pipeline Optimization";
  * P2, section 3.1; P3, section 3.1].
@@ -150,6 +151,32 @@ int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* sco
  * Supported: 1 <= K <= 2048.  No workspace.                                     */
 int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, int32_t order,
              int32_t* idx, float* vals, hipStream_t stream);
+
+/* Steps 1 + 2 fused — indexer scores and per-query Top-K without a score
+ * matrix in memory [P1, "Sparse Attention Pipeline Optimization" (indexer
+ * fusion); P4, section 2; P5, section 3.1].  Same result as sia_index_scores
+ * followed by sia_topk on those scores (same arguments and conventions as
+ * sia_topk for K, order, idx and vals), whichever method runs:
+ *   SIA_INDEX_TOPK_ONCHIP  (fp8 indexers only) each range of 8192 keys of a
+ *       query is scored into on-chip memory and reduced to its own best
+ *       min(K, keys) entries, which go to the workspace; a second pass selects
+ *       the query's Top-K from them.  One workgroup per (query, range): suits
+ *       decode-like batches, where every query has its own keys.
+ *   SIA_INDEX_TOPK_SCORES  scores go through a matrix in the workspace
+ *       (sia_index_scores, then sia_topk).
+ *   SIA_INDEX_TOPK_AUTO    the on-chip method for fp8 indexers when there are
+ *       at most two queries per sequence on average and at least one
+ *       (query, range) pair per compute unit; the score matrix otherwise.
+ *   ws  workspace of at least sia_workspace_size(SIA_OP_INDEX_TOPK, ...) bytes
+ *       (enough for either method), 256-byte aligned; heads and latent_dim
+ *       are ignored for this op.
+ * Errors: SIA_ERR_UNSUPPORTED for SIA_INDEX_TOPK_ONCHIP with an fp32 indexer. */
+enum { SIA_INDEX_TOPK_AUTO = 0, SIA_INDEX_TOPK_ONCHIP = 1, SIA_INDEX_TOPK_SCORES = 2 };
+int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, int32_t order, int32_t method,
+                   int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t stream);
+/* The method SIA_INDEX_TOPK_AUTO picks for these arguments (host-side only; a
+ * negative status for arguments sia_index_topk would reject).                 */
+int sia_index_topk_method(const sia_indexer_in* in, const sia_seqmap* seq);
 
 /* Step 3 — sparse MLA attention over the selected rows [P1, "Sparse Attention
  * Pipeline Optimization"; P3, section 3.2].  For each token t and head h, over
@@ -176,8 +203,9 @@ int sia_sparse_mla_prefill(const void* q, sia_dtype q_dtype, int32_t heads, cons
                            hipStream_t stream);
 
 /* The whole path in one call: scores -> Top-K -> sparse MLA [P1, "Sparse
- * Attention Pipeline Optimization" pseudo-code; P4, section 2].  Scores and
- * (when idx_out is NULL) indices live in the workspace.  Uses the split
+ * Attention Pipeline Optimization" pseudo-code; P4, section 2].  Steps 1 + 2
+ * run as sia_index_topk with SIA_INDEX_TOPK_AUTO; its scratch and (when
+ * idx_out is NULL) the indices live in the workspace.  Uses the split
  * (decode) attention when there are too few tokens to fill the GPU.
  *   idx_out [T, K] int32 or NULL; `order` as in sia_topk.                     */
 int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dtype q_dtype,

@@ -19,24 +19,9 @@
 // by the key's scale and writes one coalesced row segment per 64-key page.
 // Since scales are positive, ReLU(qs*ks*d) = qs*ks*ReLU(d), which is what makes
 // this folding exact in real arithmetic.
-#include "sia_common.hpp"
-#include "sia_internal.hpp"
+#include "index_core.hpp"
 
 namespace sia {
-
-struct IndexArgs {
-  const void* q;
-  const float* q_scale;
-  const float* w;
-  const void* k_pool;
-  const float* k_scale;
-  int q_scale_per_head;
-  int H;
-  int D;
-  SeqArgs s;
-  float* scores;
-  int64_t ld;
-};
 
 // ---------------------------------------------------------------------------
 // float32 path: small head counts / dims, one thread per key.
@@ -73,10 +58,6 @@ __global__ __launch_bounds__(256) void k_index_scores_f32(IndexArgs a) {
 // ---------------------------------------------------------------------------
 // fp8 path: MFMA 32x32x64, dim 128, HI in {32, 64}.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
 // One wave = one query row x a range of 64-key pages.
 // Lane l: nn = l % 32 (key within an N tile / head within an M tile), hh = l / 32.
 // K-step mapping (same for both operands): step st of lane half hh covers
@@ -84,14 +65,9 @@ __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
 template <int HI>
 __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_qblocks, int n_chunks,
                                                              int chunks_per_item) {
-  constexpr int MT = HI / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hh = lane >> 5, nn = lane & 31;
+  const int wave = threadIdx.x >> 6;
   const int n_ranges = (n_chunks + chunks_per_item - 1) / chunks_per_item;
   const int64_t items = (int64_t)n_qblocks * n_ranges;
-  const uint8_t* __restrict__ kpool = (const uint8_t*)a.k_pool;
-  const uint8_t* __restrict__ qbase = (const uint8_t*)a.q;
-
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     // heaviest (latest) query blocks first
     const int qb = n_qblocks - 1 - (int)(it / n_ranges);
@@ -107,77 +83,10 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
     c_end = c_end < c_vis ? c_end : c_vis;
     if (c_begin >= c_end) continue;
 
-    const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
     float* srow = a.scores + (int64_t)t * a.ld;
-
-    // key pages go through a ring of three register buffers: while page c is
-    // computed, pages c+1 and c+2 are in flight
-    auto load_page = [&](int c, v8i (&kb)[2][2], float& ks) __attribute__((always_inline)) {
-      int page = table[c];
-      page = page < 0 ? 0 : (page >= a.s.num_pages ? a.s.num_pages - 1 : page);
-      const uint8_t* pb = kpool + (int64_t)page * (kPage * 128) + 64 * hh;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint8_t* kr = pb + (32 * kt + nn) * 128;
-        kb[kt][0] = *(const v8i*)(kr);
-        kb[kt][1] = *(const v8i*)(kr + 32);
-      }
-      ks = a.k_scale[(int64_t)page * kPage + lane];
-    };
-    v8i k0[2][2], k1[2][2], k2[2][2];
-    float ks0 = 0.f, ks1 = 0.f, ks2 = 0.f;
-    load_page(c_begin, k0, ks0);
-    if (c_begin + 1 < c_end) load_page(c_begin + 1, k1, ks1);
-    if (c_begin + 2 < c_end) load_page(c_begin + 2, k2, ks2);
-
-    // query operand (A): head m = 32*mt + nn
-    v8i qa[MT][2];
-    float wr[MT][16];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint8_t* qr = qbase + ((int64_t)t * HI + 32 * mt + nn) * 128 + 64 * hh;
-      qa[mt][0] = *(const v8i*)(qr);
-      qa[mt][1] = *(const v8i*)(qr + 32);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int head = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const float qs = a.q_scale_per_head ? a.q_scale[(int64_t)t * HI + head] : a.q_scale[t];
-        wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
-      }
-    }
-    // scores of page c from buffer kb, then buffer kb takes page c+3
-    auto step = [&](int c, v8i (&kb)[2][2], float& ks) __attribute__((always_inline)) {
-      float p[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float sum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v16f acc = {};
-          acc = mfma_f8(qa[mt][0], kb[kt][0], acc);
-          acc = mfma_f8(qa[mt][1], kb[kt][1], acc);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sum = fmaf(wr[mt][r], fmaxf(acc[r], 0.f), sum);
-        }
-        p[kt] = sum;
-      }
-      // lane half hh keeps key tile hh; lane l ends with key 64*c + l
-      const float mine = hh ? p[1] : p[0];
-      const float give = hh ? p[0] : p[1];
-      float score = (mine + __shfl_xor(give, 32, 64)) * ks;
-      const int s = c * 64 + lane;
-      if (s > pos) score = -INFINITY;
+    score_pages<HI>(a, t, pos, b, c_begin, c_end, [&](int s, float score) __attribute__((always_inline)) {
       if (s < a.s.max_visible) srow[s] = score;
-      if (c + 3 < c_end) load_page(c + 3, kb, ks);
-    };
-    int c = c_begin;
-    for (; c + 3 <= c_end; c += 3) {
-      step(c, k0, ks0);
-      step(c + 1, k1, ks1);
-      step(c + 2, k2, ks2);
-    }
-    if (c < c_end) step(c, k0, ks0);
-    if (c + 1 < c_end) step(c + 1, k1, ks1);
+    });
   }
 }
 

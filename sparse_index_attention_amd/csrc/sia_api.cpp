@@ -105,6 +105,39 @@ static int64_t fused_ld(const sia_seqmap* s) { return ((int64_t)s->max_visible +
 
 using namespace sia;
 
+// Method of sia_index_topk chosen by SIA_INDEX_TOPK_AUTO: on-chip ranges for
+// decode-like batches (few queries per sequence) large enough to give every
+// compute unit a (query, range) workgroup.
+static int index_topk_auto(const sia_indexer_in& in, const sia_seqmap& seq) {
+  if (in.dtype != SIA_FP8_E4M3) return SIA_INDEX_TOPK_SCORES;
+  const int64_t wgs = (int64_t)seq.num_tokens * index_topk_ranges(seq.max_visible);
+  return seq.num_tokens <= 2 * seq.batch && wgs >= num_cus() ? SIA_INDEX_TOPK_ONCHIP : SIA_INDEX_TOPK_SCORES;
+}
+
+// Workspace of either method: candidate lists (scores, positions) or the score matrix.
+static size_t index_topk_ws_bytes(const sia_seqmap& seq, int K) {
+  const size_t cand = (size_t)seq.num_tokens * index_topk_ld(seq.max_visible, K);
+  const size_t onchip = 2 * align256(cand * sizeof(float));
+  const size_t matrix = align256((size_t)seq.num_tokens * fused_ld(&seq) * sizeof(float));
+  return onchip > matrix ? onchip : matrix;
+}
+
+static hipError_t run_index_topk(int method, const sia_indexer_in& in, const sia_seqmap& seq, int K, int order,
+                                 int32_t* idx, float* vals, void* ws, hipStream_t stream) {
+  const SeqArgs s = seq_args(seq);
+  if (method == SIA_INDEX_TOPK_ONCHIP) {
+    const size_t cand = (size_t)seq.num_tokens * index_topk_ld(seq.max_visible, K);
+    float* cscore = static_cast<float*>(ws);
+    int32_t* cpos = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + align256(cand * sizeof(float)));
+    return launch_index_topk(in, s, K, order, idx, vals, cscore, cpos, stream);
+  }
+  float* scores = static_cast<float*>(ws);
+  const int64_t ld = fused_ld(&seq);
+  hipError_t e = launch_index_scores(in, s, scores, ld, stream);
+  if (e == hipSuccess) e = launch_topk(scores, ld, s, K, order, idx, vals, stream);
+  return e;
+}
+
 extern "C" {
 
 const char* sia_status_string(int status) {
@@ -181,15 +214,43 @@ size_t sia_workspace_size(int32_t op, const sia_seqmap* seq, int32_t K, int32_t 
       return 0;
     case SIA_OP_MLA_DECODE:
       return mla_workspace_bytes(T, K, heads, latent_dim);
+    case SIA_OP_INDEX_TOPK:
+      return T == 0 ? 0 : index_topk_ws_bytes(*seq, K);
     case SIA_OP_INDEX_SELECT_ATTEND: {
       if (T == 0) return 0;
-      const size_t scores = align256((size_t)T * fused_ld(seq) * sizeof(float));
+      const size_t scores = index_topk_ws_bytes(*seq, K);
       const size_t ids = align256((size_t)T * K * sizeof(int32_t));
       return scores + ids + align256(mla_workspace_bytes(T, K, heads, latent_dim));
     }
     default:
       return (size_t)-1;
   }
+}
+
+int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, int32_t order, int32_t method,
+                   int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_indexer(in);
+  if (rc) return rc;
+  if (K < 1 || (order != 0 && order != 1) || !idx) return SIA_ERR_INVALID_ARG;
+  if (method < SIA_INDEX_TOPK_AUTO || method > SIA_INDEX_TOPK_SCORES) return SIA_ERR_INVALID_ARG;
+  if (K > 2048) return SIA_ERR_UNSUPPORTED;
+  if (method == SIA_INDEX_TOPK_ONCHIP && in->dtype != SIA_FP8_E4M3) return SIA_ERR_UNSUPPORTED;
+  if (seq->num_tokens == 0) return SIA_OK;
+  const size_t need = sia_workspace_size(SIA_OP_INDEX_TOPK, seq, K, 1, 1);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
+  if (method == SIA_INDEX_TOPK_AUTO) method = index_topk_auto(*in, *seq);
+  const hipError_t e = run_index_topk(method, *in, *seq, K, order, idx, vals, ws, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+int sia_index_topk_method(const sia_indexer_in* in, const sia_seqmap* seq) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_indexer(in);
+  if (rc) return rc;
+  return index_topk_auto(*in, *seq);
 }
 
 int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dtype q_dtype, int32_t heads,
@@ -208,18 +269,15 @@ int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dty
   const size_t need = sia_workspace_size(SIA_OP_INDEX_SELECT_ATTEND, seq, K, heads, kv->latent_dim);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
   const int T = seq->num_tokens;
-  const int64_t ld = fused_ld(seq);
   unsigned char* base = static_cast<unsigned char*>(ws);
-  float* scores = reinterpret_cast<float*>(base);
-  base += align256((size_t)T * ld * sizeof(float));
+  void* sel_ws = base;
+  base += index_topk_ws_bytes(*seq, K);
   int32_t* ids = idx_out ? idx_out : reinterpret_cast<int32_t*>(base);
   base += align256((size_t)T * K * sizeof(int32_t));
   void* mla_ws = base;
 
   const SeqArgs s = seq_args(*seq);
-  hipError_t e = launch_index_scores(*in, s, scores, ld, stream);
-  if (e != hipSuccess) return hip_fail(e);
-  e = launch_topk(scores, ld, s, K, order, ids, nullptr, stream);
+  hipError_t e = run_index_topk(index_topk_auto(*in, *seq), *in, *seq, K, order, ids, nullptr, sel_ws, stream);
   if (e != hipSuccess) return hip_fail(e);
   const int splits = kv->dtype == SIA_F32 ? 1 : mla_splits(T, K, heads);
   e = launch_sparse_mla(q_mla, heads, *kv, s, ids, K, softmax_scale, out, lse, splits, mla_ws, stream);

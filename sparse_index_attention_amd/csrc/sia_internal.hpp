@@ -29,8 +29,25 @@ int num_cus();
 hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,
                                hipStream_t st);
 // topk.hip
+// Candidate lists of the fused score + Top-K pass: row t holds, in ascending
+// position order, the best min(K, keys) entries of each range of range_keys
+// keys; pos[t * ld + i] is the position of entry i.  pos == nullptr: plain rows.
+struct CandMap {
+  const int32_t* pos;
+  int range_keys;
+  int K;
+};
 hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
                        float* vals, hipStream_t st);
+hipError_t launch_topk_candidates(const float* cscore, const int32_t* cpos, int64_t ldc, int range_keys,
+                                  const SeqArgs& s, int K, int order, int32_t* idx, float* vals, hipStream_t st);
+// index_topk.hip
+constexpr int kIndexTopkRangeKeys = 8192;
+int index_topk_ranges(int max_visible);
+// leading dimension of the candidate lists (a multiple of 4 floats)
+int64_t index_topk_ld(int max_visible, int K);
+hipError_t launch_index_topk(const sia_indexer_in& in, const SeqArgs& s, int K, int order, int32_t* idx,
+                             float* vals, float* cscore, int32_t* cpos, hipStream_t st);
 // sparse_mla.hip
 int mla_splits(int T, int K, int heads);
 size_t mla_workspace_bytes(int T, int K, int heads, int latent);

@@ -32,7 +32,7 @@
 // Exact path: range-adaptive radix select (<= 2048 bins per pass, three passes
 // close a 32-bit range), an ordered pass that keeps every key above the
 // threshold and the lowest-position ties, and a bitonic sort for order 0.
-#include "sia_common.hpp"
+#include "block_prims.hpp"
 #include "sia_internal.hpp"
 
 namespace sia {
@@ -46,76 +46,6 @@ constexpr int kBuf = kMaxK + kMaxBin;
 constexpr int kStreamWords = 8192;  // order-1 bitmap of streamed rows: 262144 positions
 constexpr int kDirect = 4096;
 
-// ---- wave / block primitives ------------------------------------------------
-struct OpAdd {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
-};
-struct OpMin {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
-};
-struct OpMax {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
-};
-
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint32_t dpp(uint32_t id, uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWMASK, 0xf, false);
-}
-// Inclusive scan inside each row of 16 lanes (row_shr 1, 2, 4, 8).
-template <typename Op>
-__device__ __forceinline__ uint32_t row_incl(uint32_t v, uint32_t id, Op op) {
-  v = op(v, dpp<0x111, 0xf>(id, v));
-  v = op(v, dpp<0x112, 0xf>(id, v));
-  v = op(v, dpp<0x114, 0xf>(id, v));
-  v = op(v, dpp<0x118, 0xf>(id, v));
-  return v;
-}
-// Inclusive scan over the wave in lane order (rows joined with row_bcast 15/31).
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_incl(uint32_t v, uint32_t id, Op op) {
-  v = row_incl(v, id, op);
-  v = op(v, dpp<0x142, 0xa>(id, v));
-  v = op(v, dpp<0x143, 0xc>(id, v));
-  return v;
-}
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_all(uint32_t v, uint32_t id, Op op) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl(v, id, op), 63);
-}
-__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
-
-// Combines one value per wave (slot[kNW], written before the last barrier).
-template <typename Op>
-__device__ __forceinline__ uint32_t waves_all(const uint32_t* slot, uint32_t id, Op op) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t x = lane < kNW ? slot[lane] : id;
-  return (uint32_t)__builtin_amdgcn_readlane((int)row_incl(x, id, op), kNW - 1);
-}
-
-// Exclusive prefix sum over the block in thread order, and the block total.
-// One barrier inside; `slot` (kNW words) must not be written again before the
-// next barrier that every thread passes after this call.
-__device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t* slot, uint32_t& total) {
-  const int lane = threadIdx.x & 63, w = wave_index();
-  const uint32_t inc = wave_incl(v, 0u, OpAdd{});
-  if (lane == 63) slot[w] = inc;
-  __syncthreads();
-  const uint32_t x = row_incl(lane < kNW ? slot[lane] : 0u, 0u, OpAdd{});
-  const uint32_t before = w ? (uint32_t)__builtin_amdgcn_readlane((int)x, w - 1) : 0u;
-  total = (uint32_t)__builtin_amdgcn_readlane((int)x, kNW - 1);
-  return before + inc - v;
-}
-
-// Shift that maps a key range of `range` values onto at most kBins bins.
-__device__ __forceinline__ int bin_shift(uint64_t range) {
-  const int bits = range > 1 ? 64 - __clzll((long long)(range - 1)) : 0;
-  return bits > 11 ? bits - 11 : 0;
-}
-
-__device__ __forceinline__ uint64_t composite(uint32_t key, int pos) {
-  return ((uint64_t)(~key) << 32) | (uint32_t)pos;
-}
-
 // ---- exact path ----------------------------------------------------------------
 struct ExactSmem {
   uint32_t hist[kBins];
@@ -127,7 +57,8 @@ struct ExactSmem {
 
 // Writes out[0 .. min(K, n)) for one row, reading the scores from memory.
 __device__ __noinline__ void topk_exact(const float* __restrict__ row, int n, int K, int order,
-                                        int32_t* __restrict__ orow, float* __restrict__ vrow, ExactSmem& sh) {
+                                        int32_t* __restrict__ orow, float* __restrict__ vrow,
+                                        const int32_t* __restrict__ pmap, ExactSmem& sh) {
   __syncthreads();  // every thread is done with the fast path's shared state
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index();
   int pp = 0;  // ping-pong between the two scan slots
@@ -148,8 +79,8 @@ __device__ __noinline__ void topk_exact(const float* __restrict__ row, int n, in
       sh.red[1][w] = kmx;
     }
     __syncthreads();
-    kmn = waves_all(sh.red[0], 0xffffffffu, OpMin{});
-    kmx = waves_all(sh.red[1], 0u, OpMax{});
+    kmn = waves_all<kNW>(sh.red[0], 0xffffffffu, OpMin{});
+    kmx = waves_all<kNW>(sh.red[1], 0u, OpMax{});
 
     // 2. threshold key: narrow [lo, lo + range) to the bin holding the K-th key
     uint32_t lo = kmn;
@@ -169,7 +100,7 @@ __device__ __noinline__ void topk_exact(const float* __restrict__ row, int n, in
       const int hb = kBins - 1 - 2 * tid;
       const uint32_t c0 = hb < nb ? sh.hist[hb] : 0u, c1 = hb - 1 < nb ? sh.hist[hb - 1] : 0u;
       uint32_t tot;
-      const uint32_t a0 = block_excl(c0 + c1, sh.scan[pp], tot);
+      const uint32_t a0 = block_excl<kNW>(c0 + c1, sh.scan[pp], tot);
       pp ^= 1;
       const uint32_t a1 = a0 + c0;
       if (a0 < need && need <= a0 + c0) {
@@ -206,7 +137,7 @@ __device__ __noinline__ void topk_exact(const float* __restrict__ row, int n, in
       cnt_eq += (i < n) && kk[j] == T && need > 0;
     }
     uint32_t tot;
-    const uint32_t pre = block_excl(cnt_gt | (cnt_eq << 16), sh.scan[pp], tot);
+    const uint32_t pre = block_excl<kNW>(cnt_gt | (cnt_eq << 16), sh.scan[pp], tot);
     pp ^= 1;
     uint32_t g = run_gt + (pre & 0xffffu), e = run_eq + (pre >> 16);
 #pragma unroll
@@ -252,7 +183,8 @@ __device__ __noinline__ void topk_exact(const float* __restrict__ row, int n, in
   // order 1 keeps the selection pass's ascending position order
   for (int i = tid; i < cnt; i += kNT) {
     const uint64_t v = sh.sel[i];
-    orow[i] = (int32_t)(uint32_t)v;
+    const int p = (int)(uint32_t)v;
+    orow[i] = pmap ? pmap[p] : p;
     if (vrow) vrow[i] = key2f(~(uint32_t)(v >> 32));
   }
 }
@@ -312,16 +244,28 @@ __device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1
 // the row from memory on every pass.
 template <int PER>
 __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, int64_t ld, SeqArgs s, int K,
-                                              int order, int32_t* __restrict__ idx, float* __restrict__ vals) {
+                                              int order, int32_t* __restrict__ idx, float* __restrict__ vals,
+                                              CandMap cm) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   TopkSmem<PER>& smem = *reinterpret_cast<TopkSmem<PER>*>(smem_raw);
   FastSmem<PER>& sh = smem.f;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_index();
   const int t = s.T - 1 - (int)blockIdx.x;  // longest rows first when positions grow with t
-  const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
-  const int pos = clampi(s.q_pos[t], -1, (int)lim - 1);
-  const int n = pos + 1;
+  int n;
+  const int32_t* pmap = nullptr;
+  if (cm.pos) {
+    // candidate list of a fused score + Top-K pass: every range but the last
+    // contributes exactly cm.K entries (see index_topk.hip)
+    const int nk = clampi(s.q_pos[t], -1, s.max_visible - 1) + 1;
+    const int R = (nk + cm.range_keys - 1) / cm.range_keys;
+    const int last = nk - (R - 1) * cm.range_keys;
+    n = R ? (R - 1) * cm.K + (last < cm.K ? last : cm.K) : 0;
+    pmap = cm.pos + (int64_t)t * ld;
+  } else {
+    const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
+    n = clampi(s.q_pos[t], -1, (int)lim - 1) + 1;
+  }
   const float* row = scores + (int64_t)t * ld;
   int32_t* orow = idx + (int64_t)t * K;
   float* vrow = vals ? vals + (int64_t)t * K : nullptr;
@@ -334,7 +278,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   if (sel <= 0) return;
   const int words = (n + 31) >> 5;
   if (order == 1 && words > FastSmem<PER>::kWords) {
-    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    topk_exact(row, n, K, order, orow, vrow, pmap, smem.x);
     return;
   }
 
@@ -392,11 +336,11 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
     sh.red[2][w] = wns;
   }
   __syncthreads();
-  const uint32_t kmin = waves_all(sh.red[0], 0xffffffffu, OpMin{});
-  const uint32_t kmax = waves_all(sh.red[1], 0u, OpMax{});
-  const uint32_t nsamp = waves_all(sh.red[2], 0u, OpAdd{});
+  const uint32_t kmin = waves_all<kNW>(sh.red[0], 0xffffffffu, OpMin{});
+  const uint32_t kmax = waves_all<kNW>(sh.red[1], 0u, OpMax{});
+  const uint32_t nsamp = waves_all<kNW>(sh.red[2], 0u, OpAdd{});
   if (kmax < kmin) {  // no finite score in the row
-    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    topk_exact(row, n, K, order, orow, vrow, pmap, smem.x);
     return;
   }
   const int hb = kBins - 1 - 2 * tid;  // this thread's two bins, counted from the top
@@ -412,7 +356,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
     __syncthreads();
     const uint32_t c0 = sh.hs[hb], c1 = sh.hs[hb - 1];
     uint32_t tot;
-    const uint32_t a0 = block_excl(c0 + c1, sh.scan[0], tot);
+    const uint32_t a0 = block_excl<kNW>(c0 + c1, sh.scan[0], tot);
     const uint32_t a1 = a0 + c0;
     if (a0 < r && r <= a0 + c0) sh.L = kmin + ((uint32_t)hb << shs);
     if (a1 < r && r <= a1 + c1) sh.L = kmin + ((uint32_t)(hb - 1) << shs);
@@ -430,7 +374,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   uint32_t cand;
   {
     const uint32_t m0 = sh.hist[hb], m1 = sh.hist[hb - 1];
-    const uint32_t a0 = block_excl(m0 + m1, sh.scan[1], cand);
+    const uint32_t a0 = block_excl<kNW>(m0 + m1, sh.scan[1], cand);
     const uint32_t a1 = a0 + m0;
     sh.above[hb] = a0;
     sh.above[hb - 1] = a1;
@@ -448,13 +392,13 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   }
   __syncthreads();
   if (cand < usel) {
-    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    topk_exact(row, n, K, order, orow, vrow, pmap, smem.x);
     return;
   }
   const uint32_t bstar = sh.bstar, estar = sh.estar;
-  const uint32_t maxm = waves_all(sh.maxm, 0u, OpMax{});
+  const uint32_t maxm = waves_all<kNW>(sh.maxm, 0u, OpMax{});
   if (estar > (uint32_t)kBuf || maxm > (uint32_t)kMaxBin) {
-    topk_exact(row, n, K, order, orow, vrow, smem.x);
+    topk_exact(row, n, K, order, orow, vrow, pmap, smem.x);
     return;
   }
 
@@ -477,7 +421,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
     if (fin < usel) {
       const int p = (int)(uint32_t)v;
       if (order == 0) {
-        orow[fin] = p;
+        orow[fin] = pmap ? pmap[p] : p;
         if (vrow) vrow[fin] = key2f(k);
       } else {
         atomicOr(&sh.bitmap[p >> 5], 1u << (p & 31));
@@ -494,7 +438,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   for (int i = 0; i < wpt; ++i)
     if (w0 + i < words) c += __popc(sh.bitmap[w0 + i]);
   uint32_t tot;
-  uint32_t off = block_excl(c, sh.scan[2], tot);
+  uint32_t off = block_excl<kNW>(c, sh.scan[2], tot);
   for (int i = 0; i < wpt; ++i) {
     if (w0 + i >= words) break;
     uint32_t bits = sh.bitmap[w0 + i];
@@ -502,7 +446,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
       const int bpos = __ffs(bits) - 1;
       bits &= bits - 1;
       const int p = (w0 + i) * 32 + bpos;
-      orow[off] = p;
+      orow[off] = pmap ? pmap[p] : p;
       if (vrow) vrow[off] = key2f(f2key(row[p]));
       ++off;
     }
@@ -511,11 +455,11 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
 
 template <int PER>
 static hipError_t launch_rows(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
-                              float* vals, hipStream_t st) {
+                              float* vals, const CandMap& cm, hipStream_t st) {
   const size_t shm = sizeof(TopkSmem<PER>);
   hipError_t e = hipFuncSetAttribute((const void*)k_topk<PER>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk<PER>, dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals);
+  hipLaunchKernelGGL(k_topk<PER>, dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals, cm);
   return hipGetLastError();
 }
 
@@ -523,10 +467,21 @@ hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K,
                        float* vals, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
-  if (lim <= kNT * 8) return launch_rows<8>(scores, ld, s, K, order, idx, vals, st);
-  if (lim <= kNT * 32) return launch_rows<32>(scores, ld, s, K, order, idx, vals, st);
-  if (lim <= kNT * 64) return launch_rows<64>(scores, ld, s, K, order, idx, vals, st);
-  return launch_rows<0>(scores, ld, s, K, order, idx, vals, st);
+  const CandMap none{nullptr, 0, 0};
+  if (lim <= kNT * 8) return launch_rows<8>(scores, ld, s, K, order, idx, vals, none, st);
+  if (lim <= kNT * 32) return launch_rows<32>(scores, ld, s, K, order, idx, vals, none, st);
+  if (lim <= kNT * 64) return launch_rows<64>(scores, ld, s, K, order, idx, vals, none, st);
+  return launch_rows<0>(scores, ld, s, K, order, idx, vals, none, st);
+}
+
+hipError_t launch_topk_candidates(const float* cscore, const int32_t* cpos, int64_t ldc, int range_keys,
+                                  const SeqArgs& s, int K, int order, int32_t* idx, float* vals, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  const CandMap cm{cpos, range_keys, K};
+  if (ldc <= kNT * 8) return launch_rows<8>(cscore, ldc, s, K, order, idx, vals, cm, st);
+  if (ldc <= kNT * 32) return launch_rows<32>(cscore, ldc, s, K, order, idx, vals, cm, st);
+  if (ldc <= kNT * 64) return launch_rows<64>(cscore, ldc, s, K, order, idx, vals, cm, st);
+  return launch_rows<0>(cscore, ldc, s, K, order, idx, vals, cm, st);
 }
 
 }  // namespace sia

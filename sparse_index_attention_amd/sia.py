@@ -17,7 +17,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsia.so"
 _lib = None
 
 SIA_F32, SIA_BF16, SIA_FP8_E4M3 = 0, 1, 2
-OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_INDEX_SELECT_ATTEND = 0, 1, 2, 3
+OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_INDEX_SELECT_ATTEND, OP_INDEX_TOPK = 0, 1, 2, 3, 4
+INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP, INDEX_TOPK_SCORES = 0, 1, 2
 
 c_i32, c_i64, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
@@ -56,6 +57,9 @@ def lib():
         P = ctypes.POINTER
         L.sia_index_scores.argtypes = [P(IndexerC), P(SeqMapC), c_p, c_i64, c_p]
         L.sia_topk.argtypes = [c_p, c_i64, P(SeqMapC), c_i32, c_i32, c_p, c_p, c_p]
+        L.sia_index_topk_method.argtypes = [P(IndexerC), P(SeqMapC)]
+        L.sia_index_topk.argtypes = [P(IndexerC), P(SeqMapC), c_i32, c_i32, c_i32, c_p, c_p, c_p, ctypes.c_size_t,
+                                     c_p]
         mla = [c_p, ctypes.c_int, c_i32, P(KvC), P(SeqMapC), c_p, c_i32, ctypes.c_float, c_p, c_p, c_p,
                ctypes.c_size_t, c_p]
         L.sia_sparse_mla_decode.argtypes = mla
@@ -201,6 +205,32 @@ def topk(scores: torch.Tensor, seq: SeqMap, K: int, order: int = 0, idx=None, va
     _check(lib().sia_topk(_ptr(scores), scores.shape[1], ctypes.byref(s), K, order, _ptr(idx), _ptr(vals),
                           _stream(stream)))
     return (idx, vals) if with_vals else idx
+
+
+def index_topk(ix: Indexer, seq: SeqMap, K: int, order: int = 0, method: int = 0, idx=None, vals=None,
+               with_vals=False, ws=None, stream=None):
+    """Indexer scores and Top-K in one call: same result as topk(index_scores(ix, seq), seq, K, order).
+    method: INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP or INDEX_TOPK_SCORES."""
+    T = seq.num_tokens
+    dev = ix.q.device
+    if idx is None:
+        idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    if with_vals and vals is None:
+        vals = torch.empty(T, K, dtype=torch.float32, device=dev)
+    ws = _workspace(ws, workspace_size(OP_INDEX_TOPK, seq, K, 1, 1), dev)
+    a, s = ix.c(), seq.c()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().sia_index_topk(ctypes.byref(a), ctypes.byref(s), K, order, method, _ptr(idx), _ptr(vals), _ptr(ws),
+                                nbytes, _stream(stream)))
+    return (idx, vals) if with_vals else idx
+
+
+def index_topk_method(ix: Indexer, seq: SeqMap) -> str:
+    """Name of the method index_topk's INDEX_TOPK_AUTO runs for these arguments."""
+    a, s = ix.c(), seq.c()
+    m = lib().sia_index_topk_method(ctypes.byref(a), ctypes.byref(s))
+    _check(min(m, 0))
+    return {INDEX_TOPK_ONCHIP: "onchip", INDEX_TOPK_SCORES: "scores"}[m]
 
 
 def _mla(fn, op, q, kv: LatentKV, seq: SeqMap, idx, K, softmax_scale, out, lse, ws, stream):

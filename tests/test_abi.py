@@ -39,7 +39,7 @@ def Lcpu(L):
 
 def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for f in ("sia_index_scores", "sia_topk", "sia_sparse_mla_decode", "sia_sparse_mla_prefill",
+    for f in ("sia_index_scores", "sia_topk", "sia_index_topk", "sia_sparse_mla_decode", "sia_sparse_mla_prefill",
               "sia_index_select_attend", "sia_workspace_size", "sia_status_string"):
         assert f in fns
 
@@ -118,6 +118,43 @@ def test_topk_validation(Lcpu):
     assert f(2049) == -2
     assert f(16, order=2) == -1
     assert f(16, idx=0) == -1
+
+
+def test_index_topk_validation(Lcpu):
+    L = Lcpu
+    seq = good_seq()
+    need = L.sia_workspace_size(sia.OP_INDEX_TOPK, ctypes.byref(seq), 16, 1, 1)
+    assert need > 0
+
+    def f(K=16, order=0, idx=FAKE, ws=FAKE, ws_bytes=need, ix=None, method=0):
+        return L.sia_index_topk(ctypes.byref(ix or good_indexer()), ctypes.byref(seq), K, order, method,
+                                ctypes.c_void_p(idx), None, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    assert f(K=0) == -1
+    assert f(K=2049) == -2
+    assert f(order=2) == -1
+    assert f(idx=0) == -1
+    assert f(ws=0) == -3
+    assert f(ws_bytes=need - 1) == -3
+    assert f(ws=FAKE + 16) == -3                                   # not 256-byte aligned
+    assert f(ix=good_indexer(heads=48)) == -2
+    assert f(method=3) == -1
+    assert f(method=-1) == -1
+    assert f(method=sia.INDEX_TOPK_ONCHIP, ix=good_indexer(dtype=sia.SIA_F32, heads=4, dim=32)) == -2
+
+
+def test_index_topk_method_choice(Lcpu):
+    L = Lcpu
+    m = lambda ix, seq: L.sia_index_topk_method(ctypes.byref(ix), ctypes.byref(seq))
+    f32 = good_indexer(dtype=sia.SIA_F32, heads=4, dim=32)
+    # one query per sequence and enough (query, range) pairs: on chip
+    decode = good_seq(num_tokens=4096, batch=4096, max_pages=512, num_pages=4096, max_visible=32768)
+    assert m(good_indexer(), decode) == sia.INDEX_TOPK_ONCHIP
+    assert m(f32, decode) == sia.INDEX_TOPK_SCORES
+    # many queries per sequence (prefill), or too few pairs to fill the GPU: score matrix
+    assert m(good_indexer(), good_seq(num_tokens=65536, batch=1, max_pages=1024, num_pages=1024,
+                                      max_visible=65536)) == sia.INDEX_TOPK_SCORES
+    assert m(good_indexer(), good_seq(num_tokens=2, batch=2)) == sia.INDEX_TOPK_SCORES
+    assert m(good_indexer(), good_seq(page_size=32)) == -2
 
 
 def mla_call(L, fn, kv, heads=128, K=64, scale=0.04, ws=None, ws_bytes=0, q_dtype=sia.SIA_BF16, seq=None):

@@ -71,6 +71,15 @@ def test_full_size(name):
     del out, idx, lse
     torch.cuda.empty_cache()
 
+    # steps 1 + 2: the on-chip method and the score-matrix method agree exactly
+    if wl.cfg["kind"] == "decode":
+        a_ids, a_vals = sia.index_topk(ix, seq, K, method=sia.INDEX_TOPK_ONCHIP, with_vals=True)
+        b_ids, b_vals = sia.index_topk(ix, seq, K, method=sia.INDEX_TOPK_SCORES, with_vals=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a_ids, b_ids) and torch.equal(a_vals, b_vals), "index_topk methods differ"
+        del a_ids, a_vals, b_ids, b_vals
+        torch.cuda.empty_cache()
+
     # standalone scores on the sampled rows only
     print(f"[full] {name}: oracle on {len(rows)} rows", flush=True)
     ss = sub_seq(seq, wl, rows)

@@ -288,3 +288,84 @@ def test_sparse_mla_wide_logit_range(name):
         out = fn(q, kv, seq, idx, K, scale, lse=lse)
         torch.cuda.synchronize()
         check_attention(kind_of(wl), to_np_out(out), lse.cpu().numpy(), att, range(wl.Tq))
+
+
+# ---------------------------------------------------------------------------
+# Indexer scores + Top-K in one call (scores never leave the chip on fp8 paths)
+
+def _unfused_topk(ix, seq, K, order):
+    sc = sia.index_scores(ix, seq)
+    idx, vals = sia.topk(sc, seq, K, order=order, with_vals=True)
+    return sc, idx, vals
+
+
+@pytest.mark.parametrize("name", TINY)
+@pytest.mark.parametrize("order", [0, 1])
+def test_index_topk_matches_scores_then_topk(name, order):
+    """Same ids and values as sia_index_scores followed by sia_topk."""
+    wl = workload(name)
+    print(f"[index-topk] {name} order={order}", flush=True)
+    K = wl.cfg["K"]
+    seq, ix, _, _ = upload(wl)
+    _, e_idx, e_vals = _unfused_topk(ix, seq, K, order)
+    methods = [sia.INDEX_TOPK_AUTO, sia.INDEX_TOPK_SCORES]
+    if wl.cfg["idx_dtype"] == "fp8":
+        methods.append(sia.INDEX_TOPK_ONCHIP)
+    for m in methods:
+        g_idx, g_vals = sia.index_topk(ix, seq, K, order=order, method=m, with_vals=True)
+        torch.cuda.synchronize()
+        assert torch.equal(g_idx, e_idx), f"method {m}"
+        assert torch.equal(g_vals, e_vals), f"method {m}"
+    # and against the oracle's own selection, up to ties within the score tolerance
+    sc, sel, _ = oracle_run(name)
+    ids = g_idx.cpu().numpy()
+    for t in range(wl.Tq):
+        assert tie_band_ok(sc[t], K, ids[t], sel[t]), f"row {t}"
+
+
+def _long_indexer(seed, lens, distinct, Hi=64):
+    """One query at the end of each sequence; key rows drawn from `distinct`
+    e4m3 rows (0: every row independent), so scores tie across whole ranges."""
+    rng = np.random.default_rng(seed)
+    pages = [(n + 63) // 64 for n in lens]
+    P = sum(pages)
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.zeros((len(lens), max(pages)), np.int32)
+    o = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[o:o + n]
+        o += n
+    if distinct:
+        base = W.to_e4m3(rng.standard_normal((distinct, 128)))
+        k = base[rng.integers(0, distinct, size=(P, 64))]
+        ks = np.ones((P, 64), np.float32)
+    else:
+        k = W.to_e4m3(rng.standard_normal((P, 64, 128)))
+        ks = rng.uniform(0.5, 2.0, (P, 64)).astype(np.float32)
+    T = len(lens)
+    q = W.to_e4m3(rng.standard_normal((T, Hi, 128)))
+    qs = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    w = rng.random((T, Hi)).astype(np.float32)
+    seq = sia.SeqMap(dev(np.arange(T, dtype=np.int32)), dev(np.array(lens, np.int32) - 1), dev(table), P,
+                     max(lens))
+    return seq, sia.Indexer(dev(q), dev(w), dev(k), dev(qs), dev(ks))
+
+
+@pytest.mark.parametrize("distinct", [3, 0])
+@pytest.mark.parametrize("K", [1, 100, 2048])
+@pytest.mark.parametrize("order", [0, 1])
+def test_index_topk_across_ranges(distinct, K, order):
+    """Rows spanning several 8192-key ranges, ragged last ranges, rows shorter
+    than K, and exact ties across range boundaries (lowest positions win)."""
+    print(f"[index-topk-long] distinct={distinct} K={K} order={order}", flush=True)
+    lens = [1, 64, 2047, 8191, 8192, 8193, 16389, 40000]
+    seq, ix = _long_indexer(1000 + distinct, lens, distinct)
+    sc, e_idx, e_vals = _unfused_topk(ix, seq, K, order)
+    g_idx, g_vals = sia.index_topk(ix, seq, K, order=order, method=sia.INDEX_TOPK_ONCHIP, with_vals=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g_idx, e_idx)
+    assert torch.equal(g_vals, e_vals)
+    # the selection rule itself, on the GPU's scores
+    sc, ids = sc.cpu().numpy(), g_idx.cpu().numpy()
+    for t, n in enumerate(lens):
+        assert np.array_equal(ids[t], O.topk_row(sc[t, :n], K, order)), f"row {t} (n={n})"
