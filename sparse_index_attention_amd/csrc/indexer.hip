@@ -19,6 +19,7 @@
 // by the key's scale and writes one coalesced row segment per 64-key page.
 // Since scales are positive, ReLU(qs*ks*d) = qs*ks*ReLU(d), which is what makes
 // this folding exact in real arithmetic.
+#include "block_prims.hpp"
 #include "index_core.hpp"
 
 namespace sia {
@@ -90,6 +91,176 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 path, several queries per sequence (prefill): the kSQ queries of a
+// workgroup share each key page through LDS instead of each wave reading it
+// from the cache hierarchy on its own.  One workgroup = kSQ consecutive
+// queries x a chunk of kSChunk pages; chunks run in order across the grid, so
+// the chunk in flight stays in every L2.  A workgroup whose queries belong to
+// different sequences lets each wave score its own query's pages.
+// ---------------------------------------------------------------------------
+constexpr int kSQ = 4;
+constexpr int kSChunk = 64;
+constexpr int kSThreads = 64 * kSQ;
+
+// Byte offset of 16-byte chunk j (0..7) of key row r in an LDS page: chunk j
+// is stored at j ^ ((r >> 1) & 7), so the 16 lanes of one read phase (rows
+// r..r+15 at the same j) fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kswz(int r, int j) { return r * 128 + 16 * (j ^ ((r >> 1) & 7)); }
+
+struct KStage {  // one thread's share of a key page in flight: 32 bytes and a scale
+  uint4 x, y;
+  float s;
+};
+
+template <int HI>
+__global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexArgs a, int n_qblocks) {
+  constexpr int MT = HI / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t kl[2][kPage * 128];
+  __shared__ float kls[2][kPage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int hh = lane >> 5, nn = lane & 31;
+  const int ch = (int)blockIdx.x / n_qblocks;
+  const int t0 = (n_qblocks - 1 - (int)blockIdx.x % n_qblocks) * kSQ;
+
+  // The block's queries (the same values in every thread).  Queries of one
+  // sequence share its pages; a block that spans sequences takes one round per
+  // sequence, in which only that sequence's waves compute.
+  const int nq = min(kSQ, a.s.T - t0);
+  int qseq[kSQ], cvis[kSQ], cmax = 0;
+#pragma unroll
+  for (int i = 0; i < kSQ; ++i) {
+    qseq[i] = i < nq ? clampi(a.s.q_seq[t0 + i], 0, a.s.batch - 1) : -1;
+    cvis[i] = i < nq ? (clampi(a.s.q_pos[t0 + i], -1, a.s.max_visible - 1) >> 6) + 1 : 0;
+    cmax = max(cmax, cvis[i]);
+  }
+  const int c_begin = ch * kSChunk;
+  if (c_begin >= cmax) return;
+
+  const int t = t0 + wave;
+  const bool has_q = wave < nq;
+  const int pos = has_q ? clampi(a.s.q_pos[t], -1, a.s.max_visible - 1) : -1;
+  const int my_seq = has_q ? clampi(a.s.q_seq[t], 0, a.s.batch - 1) : -1;
+  const int c_own = (pos >> 6) + 1;
+  float* srow = a.scores + (int64_t)(has_q ? t : 0) * a.ld;
+  const uint8_t* __restrict__ kpool = (const uint8_t*)a.k_pool;
+  const int sr = tid >> 2, sj = 2 * (tid & 3);  // thread moves row sr, chunks sj and sj+1
+
+  // ---- this wave's query (operand A) and folded head weights
+  v8i qa[MT][2];
+  float wr[MT][16];
+  if (has_q) {
+    const uint8_t* __restrict__ qbase = (const uint8_t*)a.q;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint8_t* qr = qbase + ((int64_t)t * HI + 32 * mt + nn) * 128 + 64 * hh;
+      qa[mt][0] = *(const v8i*)(qr);
+      qa[mt][1] = *(const v8i*)(qr + 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int head = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float qs = a.q_scale_per_head ? a.q_scale[(int64_t)t * HI + head] : a.q_scale[t];
+        wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
+      }
+    }
+  }
+
+  // scores of page c from LDS buffer `cur` (same arithmetic as score_pages)
+  auto compute = [&](int c, int cur) __attribute__((always_inline)) {
+    v8i kb[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int r = 32 * kt + nn;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int j0 = 4 * hh + 2 * st;
+        const uint4 lo = *(const uint4*)&kl[cur][kswz(r, j0)];
+        const uint4 hi = *(const uint4*)&kl[cur][kswz(r, j0 + 1)];
+        kb[kt][st] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+    const float ks = kls[cur][lane];
+    float p[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        v16f acc = {};
+        acc = mfma_f8(qa[mt][0], kb[kt][0], acc);
+        acc = mfma_f8(qa[mt][1], kb[kt][1], acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum = fmaf(wr[mt][r], __int_as_float(max(__float_as_int(acc[r]), 0)), sum);
+      }
+      p[kt] = sum;
+    }
+    const float mine = hh ? p[1] : p[0];
+    const float give = hh ? p[0] : p[1];
+    float score = (mine + __shfl_xor(give, 32, 64)) * ks;
+    const int s = c * 64 + lane;
+    if (s > pos) score = -INFINITY;
+    if (s < a.s.max_visible) srow[s] = score;
+  };
+
+  for (int i = 0; i < nq; ++i) {
+    int b = -1;
+#pragma unroll
+    for (int j = 0; j < kSQ; ++j) b = j == i ? qseq[j] : b;
+    b = __builtin_amdgcn_readfirstlane(b);
+    bool seen = false;
+    int ce = 0;
+#pragma unroll
+    for (int j = 0; j < kSQ; ++j) {
+      seen = seen || (j < i && qseq[j] == b);
+      ce = qseq[j] == b ? max(ce, cvis[j]) : ce;
+    }
+    if (seen) continue;
+    const int c_end = min(c_begin + kSChunk, __builtin_amdgcn_readfirstlane(ce));
+    if (c_begin >= c_end) continue;
+    const bool mine = my_seq == b;
+
+    // key pages: global -> registers (two pages ahead) -> LDS (double buffer);
+    // lane l of every wave holds the physical page of chunk page l
+    const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
+    const int pg = clampi(table[min(c_begin + lane, c_end - 1)], 0, a.s.num_pages - 1);
+    auto gload = [&](int c) __attribute__((always_inline)) {
+      const int page = __builtin_amdgcn_readlane(pg, min(c, c_end - 1) - c_begin);
+      const uint8_t* src = kpool + (int64_t)page * (kPage * 128) + sr * 128 + 16 * sj;
+      KStage g;
+      g.x = *(const uint4*)src;
+      g.y = *(const uint4*)(src + 16);
+      g.s = a.k_scale[(int64_t)page * kPage + lane];  // every wave loads it, wave 0 stores it
+      return g;
+    };
+    auto lwrite = [&](int buf, const KStage& g) __attribute__((always_inline)) {
+      *(uint4*)&kl[buf][kswz(sr, sj)] = g.x;
+      *(uint4*)&kl[buf][kswz(sr, sj + 1)] = g.y;
+      if (wave == 0) kls[buf][lane] = g.s;
+    };
+    // at step c: page c is in LDS buffer c & 1, page c+1 in one register
+    // stage, page c+2 in flight into the other
+    KStage sa = gload(c_begin), sb = gload(c_begin + 1);
+    __syncthreads();  // the previous round's reads of both buffers are done
+    lwrite(0, sa);
+    sa = gload(c_begin + 2);
+    int c = c_begin;
+    for (; c + 2 <= c_end; c += 2) {
+      __syncthreads();
+      lwrite(1, sb);
+      sb = gload(c + 3);
+      if (mine && c < c_own) compute(c, 0);
+      __syncthreads();
+      lwrite(0, sa);
+      sa = gload(c + 4);
+      if (mine && c + 1 < c_own) compute(c + 1, 1);
+    }
+    if (c < c_end) {
+      __syncthreads();
+      if (mine && c < c_own) compute(c, 0);
+    }
+  }
+}
+
 hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,
                                hipStream_t st) {
   IndexArgs a{in.q, in.q_scale, in.w, in.k_pool, in.k_scale, in.q_scale_per_head, in.heads, in.dim, s, scores, ld};
@@ -99,8 +270,19 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
     hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  const int n_qblocks = (s.T + 3) / 4;
   const int n_chunks = (s.max_visible + 63) / 64;
+  if (s.T >= kSQ * s.batch) {
+    // several queries per sequence on average: share key pages across queries
+    const int nqb = (s.T + kSQ - 1) / kSQ;
+    const int64_t grid = (int64_t)nqb * ((n_chunks + kSChunk - 1) / kSChunk);
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (in.heads == 64)
+      hipLaunchKernelGGL(k_index_scores_fp8_shared<64>, dim3((unsigned)grid), dim3(kSThreads), 0, st, a, nqb);
+    else
+      hipLaunchKernelGGL(k_index_scores_fp8_shared<32>, dim3((unsigned)grid), dim3(kSThreads), 0, st, a, nqb);
+    return hipGetLastError();
+  }
+  const int n_qblocks = (s.T + 3) / 4;
   // enough waves to keep every CU busy: split the key range of each query
   // block when there are few query blocks (decode), keep it whole otherwise
   const int cus = num_cus();

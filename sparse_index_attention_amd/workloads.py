@@ -68,6 +68,10 @@ CONFIGS = {
                                   kv_dtype="bf16"),
     "decode_h64_tiny": dict(cid=16, kind="decode", B=3, ctx=[33, 500, 1300], Hi=32, Di=128,
                             idx_dtype="fp8", K=192, H=64, Dc=512, Dr=64, kv_dtype="bf16"),
+    # batched chunked prefill: sequence b holds ctx[b] tokens, the last new[b] of them are queries
+    "chunked_prefill_tiny": dict(cid=17, kind="chunked", ctx=[300, 1000, 77, 2100, 5], new=[37, 130, 77, 9, 2],
+                                 Hi=64, Di=128, idx_dtype="fp8", K=128, H=128, Dc=512, Dr=64,
+                                 kv_dtype="bf16"),
 }
 
 
@@ -218,6 +222,11 @@ def _seqmap(cfg):
         q_pos = np.concatenate([np.arange(r * L, (r + 1) * L),
                                 np.arange((nseg - 1 - r) * L, (nseg - r) * L)]).astype(np.int32)
         q_seq = np.zeros(q_pos.shape[0], dtype=np.int32)
+    elif kind == "chunked":
+        lens = np.array(cfg["ctx"], dtype=np.int32)
+        new = cfg["new"]
+        q_seq = np.concatenate([np.full(n, b) for b, n in enumerate(new)]).astype(np.int32)
+        q_pos = np.concatenate([np.arange(L - n, L) for L, n in zip(lens, new)]).astype(np.int32)
     else:
         raise ValueError(kind)
     pages_per_seq = (lens + PAGE - 1) // PAGE

@@ -17,7 +17,7 @@ from gpu_support import (check_attention, check_scores, dev, kind_of, tie_band_o
 pytestmark = pytest.mark.gpu
 
 TINY = ["tiny_prefill", "decode_tiny", "prefill_tiny", "quant_decode_tiny", "quant_decode_tile128_tiny",
-        "cp_chunk_prefill_tiny", "decode_h64_tiny"]
+        "cp_chunk_prefill_tiny", "decode_h64_tiny", "chunked_prefill_tiny"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -369,3 +369,25 @@ def test_index_topk_across_ranges(distinct, K, order):
     sc, ids = sc.cpu().numpy(), g_idx.cpu().numpy()
     for t, n in enumerate(lens):
         assert np.array_equal(ids[t], O.topk_row(sc[t, :n], K, order)), f"row {t} (n={n})"
+
+
+def test_index_scores_independent_of_batching():
+    """A query's scores are the same bits whether it is scored with the other
+    queries of its sequence (key pages shared between them) or alone; blocks
+    of queries that span sequences included."""
+    wl = workload("chunked_prefill_tiny")
+    print("[scores-batching] chunked_prefill_tiny", flush=True)
+    seq, ix, _, _ = upload(wl)
+    ld = ld_of(wl)
+    full = sia.index_scores(ix, seq, ld=ld)
+    torch.cuda.synchronize()
+    full = full.cpu().numpy()
+    for t in [0, 1, 35, 36, 37, 38, 100, 166, 167, 168, 200, 243, 244, 245, 252, 253, 254]:
+        r = slice(t, t + 1)
+        s1 = sia.SeqMap(dev(wl.q_seq[r]), dev(wl.q_pos[r]), seq.block_table, seq.num_pages, seq.max_visible)
+        ix1 = sia.Indexer(ix.q[r].contiguous(), ix.w[r].contiguous(), ix.k_pool, ix.q_scale[r].contiguous(),
+                          ix.k_scale)
+        one = sia.index_scores(ix1, s1, ld=ld)
+        torch.cuda.synchronize()
+        n = int(wl.q_pos[t]) + 1
+        assert np.array_equal(one.cpu().numpy()[0, :n].view(np.uint32), full[t, :n].view(np.uint32)), f"row {t}"
