@@ -99,10 +99,11 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
       }
       p[kt] = sum;
     }
-    // lane half hh keeps key tile hh; lane l ends with key 64*c + l
-    const float mine = hh ? p[1] : p[0];
-    const float give = hh ? p[0] : p[1];
-    float score = (mine + __shfl_xor(give, 32, 64)) * ks;
+    // lane l < 32 holds half of the heads of keys l (p[0]) and 32+l (p[1]),
+    // lane 32+l the other half: swap the cross halves, then one add gives lane
+    // l the score of key 64*c + l
+    const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+    float score = (__uint_as_float(hv[0]) + __uint_as_float(hv[1])) * ks;
     const int s = c * 64 + lane;
     if (s > pos) score = -INFINITY;
     sink(s, score);

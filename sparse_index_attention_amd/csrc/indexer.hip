@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
 // different sequences lets each wave score its own query's pages.
 // ---------------------------------------------------------------------------
 constexpr int kSQ = 4;
-constexpr int kSChunk = 64;
+constexpr int kSChunk = 128;
+constexpr int kRawBuffer = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
 constexpr int kSThreads = 64 * kSQ;
 
 // Byte offset of 16-byte chunk j (0..7) of key row r in an LDS page: chunk j
@@ -142,7 +143,8 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
   const int pos = has_q ? clampi(a.s.q_pos[t], -1, a.s.max_visible - 1) : -1;
   const int my_seq = has_q ? clampi(a.s.q_seq[t], 0, a.s.batch - 1) : -1;
   const int c_own = (pos >> 6) + 1;
-  float* srow = a.scores + (int64_t)(has_q ? t : 0) * a.ld;
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(a.scores + (int64_t)(has_q ? t : 0) * a.ld, 0, a.s.max_visible * 4, kRawBuffer);
   const uint8_t* __restrict__ kpool = (const uint8_t*)a.k_pool;
   const int sr = tid >> 2, sj = 2 * (tid & 3);  // thread moves row sr, chunks sj and sj+1
 
@@ -194,12 +196,15 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
       }
       p[kt] = sum;
     }
-    const float mine = hh ? p[1] : p[0];
-    const float give = hh ? p[0] : p[1];
-    float score = (mine + __shfl_xor(give, 32, 64)) * ks;
-    const int s = c * 64 + lane;
-    if (s > pos) score = -INFINITY;
-    if (s < a.s.max_visible) srow[s] = score;
+    // lane l < 32 holds half of the heads of keys l (p[0]) and 32+l (p[1]),
+    // lane 32+l the other half: swap the cross halves, then one add gives lane
+    // l the score of key l
+    const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+    float score = (__uint_as_float(hv[0]) + __uint_as_float(hv[1])) * ks;
+    if (c * 64 + 63 > pos) score = c * 64 + lane > pos ? -INFINITY : score;
+    // the row's buffer ends at max_visible: the range check on the vector
+    // offset drops stores past it
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), srs, (c * 64 + lane) * 4, 0, 0);
   };
 
   for (int i = 0; i < nq; ++i) {
@@ -220,11 +225,18 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
     const bool mine = my_seq == b;
 
     // key pages: global -> registers (two pages ahead) -> LDS (double buffer);
-    // lane l of every wave holds the physical page of chunk page l
+    // lane l of pg[k] holds the physical page of chunk page 64k + l
     const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
-    const int pg = clampi(table[min(c_begin + lane, c_end - 1)], 0, a.s.num_pages - 1);
+    constexpr int NPG = kSChunk / 64;
+    int pg[NPG];
+#pragma unroll
+    for (int k = 0; k < NPG; ++k) pg[k] = clampi(table[min(c_begin + 64 * k + lane, c_end - 1)], 0, a.s.num_pages - 1);
     auto gload = [&](int c) __attribute__((always_inline)) {
-      const int page = __builtin_amdgcn_readlane(pg, min(c, c_end - 1) - c_begin);
+      const int o = min(c, c_end - 1) - c_begin;
+      int sel = pg[0];
+#pragma unroll
+      for (int k = 1; k < NPG; ++k) sel = (o >> 6) == k ? pg[k] : sel;
+      const int page = __builtin_amdgcn_readlane(sel, o & 63);
       const uint8_t* src = kpool + (int64_t)page * (kPage * 128) + sr * 128 + 16 * sj;
       KStage g;
       g.x = *(const uint4*)src;
@@ -271,7 +283,7 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
     return hipGetLastError();
   }
   const int n_chunks = (s.max_visible + 63) / 64;
-  if (s.T >= kSQ * s.batch) {
+  if (s.T >= kSQ * s.batch && s.max_visible <= (1 << 29)) {
     // several queries per sequence on average: share key pages across queries
     const int nqb = (s.T + kSQ - 1) / kSQ;
     const int64_t grid = (int64_t)nqb * ((n_chunks + kSChunk - 1) / kSChunk);

@@ -391,3 +391,24 @@ def test_index_scores_independent_of_batching():
         torch.cuda.synchronize()
         n = int(wl.q_pos[t]) + 1
         assert np.array_equal(one.cpu().numpy()[0, :n].view(np.uint32), full[t, :n].view(np.uint32)), f"row {t}"
+
+
+@pytest.mark.parametrize("name", ["prefill_tiny", "chunked_prefill_tiny", "decode_tiny", "cp_chunk_prefill_tiny"])
+def test_index_scores_never_write_past_max_visible(name):
+    """Entries at s >= max_visible of a padded score buffer keep their contents
+    (pages straddling max_visible are computed whole)."""
+    wl = workload(name)
+    print(f"[scores-bounds] {name}", flush=True)
+    seq, ix, _, _ = upload(wl)
+    mv = wl.max_visible
+    ld = (mv + 3) // 4 * 4 + 132
+    buf = torch.full((wl.Tq, ld), 12345.0, dtype=torch.float32, device="cuda")
+    sia.index_scores(ix, seq, buf)
+    torch.cuda.synchronize()
+    tail = buf[:, mv:].cpu().numpy()
+    assert np.all(tail == 12345.0), f"{int(np.sum(tail != 12345.0))} entries past max_visible written"
+    # and the visible part is written
+    got = buf.cpu().numpy()
+    for t in range(wl.Tq):
+        n = int(wl.q_pos[t]) + 1
+        assert np.all(np.isfinite(got[t, :n])), f"row {t}"
