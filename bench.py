@@ -41,7 +41,91 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-breakdown", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="after the run, launch a plain copy kernel of known size (HBM counter calibration)")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no benchmark: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                        "`bench.py --copy-probe` into profiles/<workload>_traffic.json")
     return p.parse_args()
+
+
+# HBM traffic of the dominant kernels, from FETCH_SIZE / WRITE_SIZE counters
+COPY_PROBE_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
+TRAFFIC_KERNELS = {                 # roofline kernel -> (kernel-name substrings, sources it is built from)
+    "sparse_mla": (("k_sparse_mla_mfma", "k_mla_combine"),
+                   ("sparse_mla.hip", "sia_common.hpp", "sia_internal.hpp")),
+    "index_scores": (("k_index_scores_fp8",),
+                     ("indexer.hip", "index_core.hpp", "block_prims.hpp", "sia_common.hpp", "sia_internal.hpp")),
+}
+
+
+def sources_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_index_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+
+
+def write_traffic(workload, fetch_csv, write_csv):
+    """Per-launch HBM bytes of each roofline kernel: counter KiB x (known copy
+    bytes / the copy kernel's counter KiB), averaged over the kernel's launches."""
+    import csv
+    import collections
+
+    def per_dispatch(path):
+        rows = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            d = r["Dispatch_Id"]
+            rows[d] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+        return rows, names
+
+    out = {"workload": workload, "copy_probe_bytes": COPY_PROBE_BYTES, "kernels": {}}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        vals, names = per_dispatch(path)
+        copies = [vals[d] for d in vals if "elementwise" in names[d] and "MulFunctor" in names[d]]
+        if not copies:
+            raise SystemExit(f"no calibration copy kernel in {path}")
+        factor = COPY_PROBE_BYTES / (1024.0 * sorted(copies)[len(copies) // 2])
+        out[f"{label}_factor"] = factor
+        for k, (subs, _) in TRAFFIC_KERNELS.items():
+            # one launch of `k` = one dispatch of each of its kernels that ran
+            # (the split merge runs only when rows are split): pair them up in order
+            per = [sorted((d for d in vals if s in names[d]), key=int) for s in subs]
+            per = [x for x in per if x]
+            if not per:
+                continue
+            n = min(len(x) for x in per)
+            kib = sum(vals[x[i]] for x in per for i in range(n)) / n
+            out["kernels"].setdefault(k, {})[f"{label}_bytes"] = kib * 1024.0 * factor
+            out["kernels"][k]["launches"] = n
+    for k, v in out["kernels"].items():
+        v["traffic_bytes"] = v.get("fetch_bytes", 0.0) + v.get("write_bytes", 0.0)
+        v["sources_sha256_16"] = sources_digest(TRAFFIC_KERNELS[k][1])
+    os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def measured_traffic(workload, kernel):
+    """Bytes per launch from the committed counter record, or None when there is
+    none or the kernel's sources changed since it was taken."""
+    try:
+        with open(traffic_path(workload)) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256_16") != sources_digest(TRAFFIC_KERNELS[kernel][1]):
+        return None
+    return rec["traffic_bytes"]
 
 
 def algorithmic_work(wl):
@@ -106,6 +190,9 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic(args.workload, *args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design note, "
               "not part of this build.", file=sys.stderr)
@@ -248,14 +335,25 @@ def main():
         if decode:
             achieved = by / (us * 1e-6) / 1e9
             roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(args.workload, dom),
                         "algorithmic_bytes": by, "avg_us": us}
         else:
             peak = FP8_PEAK_TFLOPS if dom == "index_scores" else BF16_PEAK_TFLOPS
             achieved = fl / (us * 1e-6) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "traffic": measured_traffic(args.workload, dom),
                         "algorithmic_flops": fl, "avg_us": us}
+
+    if args.copy_probe:
+        # calibration for the HBM byte counters: one elementwise copy of known size
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
