@@ -25,7 +25,8 @@ shared by all indexer heads; causal visibility s <= q_pos (diagonal included);
 Top-K order (score descending, position ascending) with -0 == +0; K larger than
 the visible count emits every visible position then -1; the MLA key is the whole
 latent+rope row and the value is its latent part, shared by all heads; softmax is
-exact; fp8 is OCP e4m3fn.
+exact; fp8 is OCP e4m3fn; an MXFP8 group is 32 consecutive elements of a query
+head's or a key's dim axis sharing one OCP E8M0 scale.
 
 Every function below is pinned by CPU tests against closed forms, library
 routines, brute force or invariants (see tests/test_oracle_pins.py).
@@ -35,7 +36,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "decode_e4m3", "decode_bf16", "physical_slots", "key_rows", "kv_rows",
+    "decode_e4m3", "decode_bf16", "decode_e8m0", "mx_values", "physical_slots", "key_rows", "kv_rows",
     "index_scores_row", "index_scores", "topk_row", "topk", "sparse_mla_row",
     "sparse_mla", "merge_partials", "index_select_attend",
 ]
@@ -64,6 +65,28 @@ def decode_e4m3(codes) -> np.ndarray:
     return sign * val
 
 
+def decode_e8m0(codes) -> np.ndarray:
+    """OCP E8M0 scale byte -> float64: 2^(e - 127); 0xFF is NaN.
+
+    The indexer's MXFP8 groups share one power-of-two scale ("block
+    floating-point ... shared exponent", [P2, section 4.1]; [P5, section 4
+    table]); the 8-bit exponent-only encoding is the OCP MX one (a reading:
+    the pages name MXFP8 but print no encoding).
+    """
+    e = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    val = np.ldexp(1.0, (e - 127).astype(np.int64))
+    return np.where(e == 255, np.nan, val)
+
+
+def mx_values(codes, scales, group=32) -> np.ndarray:
+    """MXFP8 block -> float64: e4m3 code x the E8M0 scale of its group of 32
+    consecutive elements along the last axis ([P1, "Hierarchical
+    Quantization"]: group size 32; [P2, section 4.1])."""
+    v = decode_e4m3(codes)
+    sc = decode_e8m0(scales)
+    return v * np.repeat(sc, group, axis=-1)
+
+
 def decode_bf16(bits) -> np.ndarray:
     """bfloat16 bit pattern (uint16) -> float64: the upper half of an IEEE float32."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
@@ -86,11 +109,17 @@ def physical_slots(block_table_row, positions, page_size) -> np.ndarray:
     return table[pos // page_size] * page_size + pos % page_size
 
 
-def key_rows(k_pool, k_scale, slots):
-    """Indexer keys at the given slots: (decoded key values [n, Di], key scales [n])."""
+def key_rows(k_pool, k_scale, slots, k_mx=None):
+    """Indexer keys at the given slots: (decoded key values [n, Di], key scales [n]).
+
+    MXFP8 keys (k_mx given, [pages, page, Di/32] E8M0 bytes) fold their group
+    scales into the values and have unit key scales."""
     D = k_pool.shape[-1]
     flat = k_pool.reshape(-1, D)[slots]
-    if k_pool.dtype == np.uint8:
+    if k_mx is not None:
+        vals = mx_values(flat, np.asarray(k_mx).reshape(-1, D // 32)[slots])
+        sc = np.ones(len(slots), dtype=np.float64)
+    elif k_pool.dtype == np.uint8:
         vals = decode_e4m3(flat)
         sc = np.asarray(k_scale, dtype=np.float64).reshape(-1)[slots]
     else:
@@ -154,7 +183,10 @@ def index_scores_row(q_row, q_scale_row, w_row, keys, k_scale) -> np.ndarray:
 
 def _q_index_row(idx, t):
     q = idx["q"][t]
-    if q.dtype == np.uint8:
+    if idx.get("q_mx") is not None:
+        qv = mx_values(q, idx["q_mx"][t])
+        qs = np.ones(q.shape[0])
+    elif q.dtype == np.uint8:
         qv = decode_e4m3(q)
         qs = np.asarray(idx["q_scale"][t], dtype=np.float64)
         qs = np.broadcast_to(qs, (q.shape[0],)) if qs.ndim == 0 else qs
@@ -168,7 +200,8 @@ def index_scores(idx, seq, rows=None) -> dict:
     """Scores for query rows `rows` (default: all).  Returns {t: float32 [q_pos[t]+1]}.
 
     idx: dict with q [Tq,Hi,Di] (uint8 codes or f32), q_scale ([Tq] or [Tq,Hi],
-    fp8 only), w [Tq,Hi], k [P,page,Di], k_scale [P,page] (fp8 only).
+    fp8 only), w [Tq,Hi], k [P,page,Di], k_scale [P,page] (fp8 only); MXFP8
+    instead gives q_mx [Tq,Hi,Di/32] and k_mx [P,page,Di/32] E8M0 bytes.
     seq: dict with q_seq, q_pos, block_table, page_size.
     Causal visibility: key s is visible to query t iff s <= q_pos[t] (a reading
     of the causal history the pages describe, [P1, "Prefill Context
@@ -181,7 +214,7 @@ def index_scores(idx, seq, rows=None) -> dict:
     for t in rows:
         b, pos = int(seq["q_seq"][t]), int(seq["q_pos"][t])
         slots = physical_slots(seq["block_table"][b], np.arange(pos + 1), seq["page_size"])
-        keys, ks = key_rows(idx["k"], idx.get("k_scale"), slots)
+        keys, ks = key_rows(idx["k"], idx.get("k_scale"), slots, idx.get("k_mx"))
         qv, qs, w = _q_index_row(idx, t)
         out[t] = index_scores_row(qv, qs, w, keys, ks).astype(np.float32)
     return out

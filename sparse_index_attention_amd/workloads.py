@@ -15,7 +15,9 @@ Tensor ids: 0 indexer q, 1 indexer k, 2 head weights, 3 MLA q, 4 latent KV,
 Distributions: indexer q/k, MLA q and latent KV ~ N(0,1); head weights ~ U(0,1).
 fp8 tensors are quantized with a dynamic scale = amax/448 over the scale group
 (amax 0 -> scale 1), codes = round-to-nearest-even(x/scale) saturated to +-448
-(OCP e4m3fn).  bf16 tensors are float32 draws rounded to nearest even.
+(OCP e4m3fn).  MXFP8 tensors take one power-of-two scale per 32 consecutive
+elements of the last axis, the smallest 2^e with amax <= 448 * 2^e, stored as
+an E8M0 byte (amax 0 -> byte 0), and the same e4m3 rounding.  bf16 tensors are float32 draws rounded to nearest even.
 Physical pages are a random permutation of the pool (shuffled block tables).
 """
 from __future__ import annotations
@@ -68,6 +70,13 @@ CONFIGS = {
                                   kv_dtype="bf16"),
     "decode_h64_tiny": dict(cid=16, kind="decode", B=3, ctx=[33, 500, 1300], Hi=32, Di=128,
                             idx_dtype="fp8", K=192, H=64, Dc=512, Dr=64, kv_dtype="bf16"),
+    # MXFP8 indexer (32-element groups with E8M0 scales), otherwise as decode / prefill
+    "mx_decode": dict(cid=5, kind="decode", B=64, ctx=32768, Hi=64, Di=128, idx_dtype="mxfp8",
+                      K=2048, H=128, Dc=512, Dr=64, kv_dtype="bf16"),
+    "mx_decode_tiny": dict(cid=18, kind="decode", B=5, ctx=[1, 64, 333, 2100, 9000], Hi=64, Di=128,
+                           idx_dtype="mxfp8", K=256, H=128, Dc=512, Dr=64, kv_dtype="bf16"),
+    "mx_prefill_tiny": dict(cid=19, kind="prefill", T=430, Hi=32, Di=128, idx_dtype="mxfp8", K=64,
+                            H=64, Dc=512, Dr=64, kv_dtype="bf16"),
     # batched chunked prefill: sequence b holds ctx[b] tokens, the last new[b] of them are queries
     "chunked_prefill_tiny": dict(cid=17, kind="chunked", ctx=[300, 1000, 77, 2100, 5], new=[37, 130, 77, 9, 2],
                                  Hi=64, Di=128, idx_dtype="fp8", K=128, H=128, Dc=512, Dr=64,
@@ -115,6 +124,8 @@ class Workload:
                     page_size=PAGE)
 
     def oracle_indexer(self):
+        if self.cfg["idx_dtype"] == "mxfp8":
+            return dict(q=self.iq, q_mx=self.iq_scale, w=self.iw, k=self.ik, k_mx=self.ik_scale)
         return dict(q=self.iq, q_scale=self.iq_scale, w=self.iw, k=self.ik, k_scale=self.ik_scale)
 
     def oracle_kv(self):
@@ -192,6 +203,22 @@ def to_e4m3(x: np.ndarray) -> np.ndarray:
     return code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
 
 
+def quantize_mx(x: np.ndarray, group: int = 32):
+    """MXFP8 along the last axis: (e4m3 codes, E8M0 scale bytes [..., n/group]).
+
+    Scale 2^e with the smallest e such that amax <= 448 * 2^e (no element
+    saturates); with amax = m * 2^E, m in [0.5, 1): e = E - 9 if m <= 0.875
+    else E - 8.  amax = 0 gives byte 0."""
+    g = x.reshape(*x.shape[:-1], x.shape[-1] // group, group).astype(np.float64)
+    amax = np.max(np.abs(g), axis=-1)
+    m, E = np.frexp(amax)
+    e = np.where(m <= 0.875, E - 9, E - 8)
+    e = np.where(amax > 0, e, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    codes = to_e4m3(g / np.ldexp(1.0, e)[..., None]).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
 def quantize_groups(x: np.ndarray, axes):
     """Dynamic fp8 quantization with one scale per group (the reduced `axes`)."""
     amax = np.max(np.abs(x), axis=axes, keepdims=True).astype(np.float32)
@@ -251,7 +278,25 @@ def make_workload(name: str, mla=True, indexer=True) -> Workload:
     Hi, Di, H, Dc, Dr = cfg["Hi"], cfg["Di"], cfg["H"], cfg["Dc"], cfg["Dr"]
 
     if indexer:
-        if cfg["idx_dtype"] == "f32":
+        if cfg["idx_dtype"] == "mxfp8":
+            qsc = np.empty((Tq, Hi, Di // 32), dtype=np.uint8)
+            ksc = np.empty((P * PAGE, Di // 32), dtype=np.uint8)
+
+            def qconv(x, r0):
+                codes, e = quantize_mx(x)
+                qsc[r0:r0 + x.shape[0]] = e
+                return codes
+
+            def kconv(x, r0):
+                codes, e = quantize_mx(x)
+                ksc[r0:r0 + x.shape[0]] = e
+                return codes
+
+            wl.iq = _draw_rows(cid, 0, Tq, (Hi, Di), "normal", convert=qconv, out_dtype=np.uint8)
+            wl.ik = _draw_rows(cid, 1, P * PAGE, (Di,), "normal", convert=kconv,
+                               out_dtype=np.uint8).reshape(P, PAGE, Di)
+            wl.iq_scale, wl.ik_scale = qsc, ksc.reshape(P, PAGE, Di // 32)
+        elif cfg["idx_dtype"] == "f32":
             wl.iq = _draw_rows(cid, 0, Tq, (Hi, Di), "normal")
             wl.ik = _draw_rows(cid, 1, P * PAGE, (Di,), "normal").reshape(P, PAGE, Di)
         else:

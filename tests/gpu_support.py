@@ -17,7 +17,7 @@ from sparse_index_attention_amd import workloads as W
 # for the fp8 MFMA path (its internal accumulation rounds at ~2^-14 of A) and
 # 2^-16 for the fp32 path.
 SCORE_REL = 1e-3
-SCORE_EPS = {"fp8": 2.0 ** -11, "f32": 2.0 ** -16}
+SCORE_EPS = {"fp8": 2.0 ** -11, "mxfp8": 2.0 ** -11, "f32": 2.0 ** -16}
 # Attention tolerance: |g - o| <= ATOL + RTOL |o| elementwise.
 ATT_TOL = {"bf16": (2e-2, 1e-2), "fp8": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
 LSE_ATOL = {"bf16": 2e-2, "fp8": 2e-2, "f32": 1e-4}
@@ -54,9 +54,11 @@ def score_bound_row(wl: W.Workload, t: int) -> np.ndarray:
     idx = wl.oracle_indexer()
     b, pos = int(wl.q_seq[t]), int(wl.q_pos[t])
     slots = O.physical_slots(wl.block_table[b], np.arange(pos + 1), W.PAGE)
-    keys, ks = O.key_rows(idx["k"], idx.get("k_scale"), slots)
+    keys, ks = O.key_rows(idx["k"], idx.get("k_scale"), slots, idx.get("k_mx"))
     q = idx["q"][t]
-    if q.dtype == np.uint8:
+    if idx.get("q_mx") is not None:
+        qv, qs = O.mx_values(q, idx["q_mx"][t]), np.ones(q.shape[0])
+    elif q.dtype == np.uint8:
         qv = O.decode_e4m3(q)
         qs = np.full(q.shape[0], float(idx["q_scale"][t]))
     else:

@@ -144,6 +144,94 @@ def test_scores_fp8_rows_use_both_scales():
         assert sc[s] == np.float32(ref)
 
 
+def test_e8m0_landmarks():
+    """Shared-scale landmarks from tests/golden/e8m0_landmarks.txt."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "e8m0_landmarks.txt")
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code, val = line.split()
+        got = O.decode_e8m0(np.array([int(code, 16)], dtype=np.uint8))[0]
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert got == float(val), (code, got, val)
+
+
+def _brute_mx_scores(qc, qe, w, kc, ke):
+    """MXFP8 scores by explicit loops: element d of a row is decode(code) *
+    2^(e[d // 32] - 127)."""
+    def val(c, e, d):
+        return float(O.decode_e4m3(np.array([c], dtype=np.uint8))[0]) * math.ldexp(1.0, int(e[d // 32]) - 127)
+    Hi, Di = qc.shape
+    out = []
+    for s in range(kc.shape[0]):
+        tot = 0.0
+        for h in range(Hi):
+            dot = math.fsum(val(qc[h, d], qe[h], d) * val(kc[s, d], ke[s], d) for d in range(Di))
+            tot += float(w[h]) * max(0.0, dot)
+        out.append(tot)
+    return np.array(out)
+
+
+def _mx_inputs(rng, Hi, n, Di=64):
+    codes = lambda shape: np.where(rng.random(shape) < 0.5, 0, 0x80).astype(np.uint8) | \
+        rng.integers(0, 0x7f, size=shape).astype(np.uint8)        # finite e4m3 codes of both signs
+    return (codes((Hi, Di)), rng.integers(110, 140, size=(Hi, Di // 32)).astype(np.uint8), rng.random(Hi),
+            codes((n, Di)), rng.integers(110, 140, size=(n, Di // 32)).astype(np.uint8))
+
+
+def test_mx_scores_brute_force_small():
+    rng = np.random.default_rng(11)
+    qc, qe, w, kc, ke = _mx_inputs(rng, 3, 7)
+    idx = dict(q=qc[None], q_mx=qe[None], w=w[None], k=kc[None], k_mx=ke[None])
+    seq = dict(q_seq=np.zeros(1, np.int32), q_pos=np.array([6], np.int32), block_table=np.zeros((1, 1), np.int64),
+               page_size=64)
+    got = O.index_scores(idx, seq)[0]
+    ref = _brute_mx_scores(qc, qe, w, kc, ke)
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_mx_with_one_exponent_per_row_is_per_token_fp8():
+    """When every group of a query head shares one exponent (and of a key), MXFP8
+    scores equal the per-token fp8 scores with those powers of two as scales."""
+    rng = np.random.default_rng(12)
+    qc, _, w, kc, _ = _mx_inputs(rng, 4, 9)
+    eq = rng.integers(120, 135, size=4)
+    ek = rng.integers(120, 135, size=9)
+    qe = np.repeat(eq[:, None], 2, axis=1).astype(np.uint8)
+    ke = np.repeat(ek[:, None], 2, axis=1).astype(np.uint8)
+    mx = O.index_scores_row(O.mx_values(qc, qe), np.ones(4), w, O.mx_values(kc, ke), np.ones(9))
+    fp8 = O.index_scores_row(O.decode_e4m3(qc), np.ldexp(1.0, eq - 127), w, O.decode_e4m3(kc), np.ldexp(1.0, ek - 127))
+    assert np.allclose(mx, fp8, rtol=1e-14, atol=0)
+
+
+def test_mx_group_scales_apply_to_their_32_elements():
+    """Raising the exponent of one group of a key doubles exactly that group's
+    contribution: q = e4m3 1.0 everywhere, k = 1.0 in group 0 and 2.0 in group 1."""
+    Di = 64
+    qc = np.full((1, Di), 0x38, np.uint8)                 # 1.0
+    kc = np.full((1, Di), 0x38, np.uint8)
+    qe = np.full((1, 2), 127, np.uint8)
+    ke = np.array([[127, 128]], np.uint8)                 # group 1 scaled by 2
+    got = O.index_scores_row(O.mx_values(qc, qe), np.ones(1), np.ones(1), O.mx_values(kc, ke), np.ones(1))
+    assert got[0] == 32 * 1.0 + 32 * 2.0
+
+
+def test_mx_generator_roundtrip():
+    """Generated MXFP8 data decodes to within one e4m3 step of the draw and never saturates."""
+    x = np.random.default_rng(13).standard_normal((200, 128)).astype(np.float32)
+    codes, e = W.quantize_mx(x)
+    back = O.mx_values(codes, e)
+    scale = np.repeat(O.decode_e8m0(e), 32, axis=-1)
+    assert np.all(np.abs(O.decode_e4m3(codes)) <= 448)
+    assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) * 2.0 ** -4, scale * 2.0 ** -9) + 1e-12)
+    amax = np.max(np.abs(x.reshape(200, 4, 32)), axis=-1)
+    s = O.decode_e8m0(e)
+    assert np.all(amax <= 448 * s) and np.all(amax > 224 * s)   # the smallest power of two that fits
+
+
 # ---------------------------------------------------------------------------
 # Top-K
 # ---------------------------------------------------------------------------
