@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill"])
+                   choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill", "mx_decode"])
     p.add_argument("--copies", type=int, default=3, help="distinct device copies of the inputs (decode)")
     p.add_argument("--order", type=int, default=0, help="Top-K output order (0 score-sorted, 1 by position)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle baseline")
@@ -136,8 +136,11 @@ def algorithmic_work(wl):
     Hi, Di, H, Dc, Dr, K = c["Hi"], c["Di"], c["H"], c["Dc"], c["Dr"], c["K"]
     vis = (wl.q_pos.astype("int64") + 1)
     sel = vis.clip(max=K)
-    key_b = Di + 4 if c["idx_dtype"] == "fp8" else 4 * Di
-    q_b = Hi * Di * (1 if c["idx_dtype"] == "fp8" else 4) + 4 * Hi + 4
+    if c["idx_dtype"] == "mxfp8":          # codes + one E8M0 byte per 32 elements
+        key_b, q_b = Di + Di // 32, Hi * (Di + Di // 32) + 4 * Hi
+    else:
+        key_b = Di + 4 if c["idx_dtype"] == "fp8" else 4 * Di
+        q_b = Hi * Di * (1 if c["idx_dtype"] == "fp8" else 4) + 4 * Hi + 4
     if c["kv_dtype"] == "bf16":
         row_b = 2 * (Dc + Dr)
     elif c["kv_dtype"] == "fp8":
@@ -372,7 +375,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2), "wall_s": round(wall, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8+bf16" if c["idx_dtype"] == "fp8" else "f32", "data": "synthetic",
+        "dtype": {"fp8": "fp8+bf16", "mxfp8": "mxfp8+bf16"}.get(c["idx_dtype"], "f32"), "data": "synthetic",
         "config": cfg, "breakdown_us": breakdown, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

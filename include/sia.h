@@ -51,7 +51,7 @@ typedef enum {
   SIA_ERR_HIP = -4          /* a HIP launch failed */
 } sia_status;
 
-typedef enum { SIA_F32 = 0, SIA_BF16 = 1, SIA_FP8_E4M3 = 2 } sia_dtype;
+typedef enum { SIA_F32 = 0, SIA_BF16 = 1, SIA_FP8_E4M3 = 2, SIA_MXFP8_E4M3 = 3 } sia_dtype;
 
 /* Query -> sequence map shared by every step.  Varlen batches are described by
  * vectors of offsets instead of per-sequence loops [P3, section 3.1].
@@ -83,20 +83,26 @@ typedef struct {
 } sia_seqmap;
 
 /* Indexer inputs [P1, "Sparse Attention Pipeline Optimization"; P2, section 3.1].
- *   q        [T, heads, dim]  fp8 codes (SIA_FP8_E4M3) or float (SIA_F32)
- *   q_scale  fp8 only: [T] (q_scale_per_head = 0) or [T, heads] (= 1)
+ *   q        [T, heads, dim]  e4m3 codes (SIA_FP8_E4M3, SIA_MXFP8_E4M3) or
+ *            float (SIA_F32)
+ *   q_scale  SIA_FP8_E4M3: float [T] (q_scale_per_head = 0) or [T, heads] (= 1)
+ *            SIA_MXFP8_E4M3: uint8 [T, heads, dim/32], one OCP E8M0 scale
+ *            (2^(e-127)) per 32 consecutive elements of a head's q [P1,
+ *            "Hierarchical Quantization"; P2, section 4.1]; 4-byte aligned
  *   w        [T, heads] float head weights
  *   k_pool   [num_pages, page_size, dim] keys, same dtype as q; one key vector
  *            per token shared by all indexer heads
- *   k_scale  fp8 only: [num_pages, page_size] float, one per key token
- * Supported: SIA_F32 with heads <= 64, dim <= 256; SIA_FP8_E4M3 with
- * heads in {32, 64} and dim = 128.                                            */
+ *   k_scale  SIA_FP8_E4M3: float [num_pages, page_size], one per key token
+ *            SIA_MXFP8_E4M3: uint8 [num_pages, page_size, dim/32] E8M0 group
+ *            scales; 4-byte aligned
+ * Supported: SIA_F32 with heads <= 64, dim <= 256; SIA_FP8_E4M3 and
+ * SIA_MXFP8_E4M3 with heads in {32, 64} and dim = 128.                        */
 typedef struct {
   const void* q;
-  const float* q_scale;
+  const void* q_scale;
   const float* w;
   const void* k_pool;
-  const float* k_scale;
+  const void* k_scale;
   sia_dtype dtype;
   int32_t q_scale_per_head;
   int32_t heads;
@@ -157,14 +163,14 @@ int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, 
  * fusion); P4, section 2; P5, section 3.1].  Same result as sia_index_scores
  * followed by sia_topk on those scores (same arguments and conventions as
  * sia_topk for K, order, idx and vals), whichever method runs:
- *   SIA_INDEX_TOPK_ONCHIP  (fp8 indexers only) each range of 8192 keys of a
+ *   SIA_INDEX_TOPK_ONCHIP  (fp8 and MXFP8 indexers) each range of 8192 keys of a
  *       query is scored into on-chip memory and reduced to its own best
  *       min(K, keys) entries, which go to the workspace; a second pass selects
  *       the query's Top-K from them.  One workgroup per (query, range): suits
  *       decode-like batches, where every query has its own keys.
  *   SIA_INDEX_TOPK_SCORES  scores go through a matrix in the workspace
  *       (sia_index_scores, then sia_topk).
- *   SIA_INDEX_TOPK_AUTO    the on-chip method for fp8 indexers when there are
+ *   SIA_INDEX_TOPK_AUTO    the on-chip method for fp8 and MXFP8 indexers when there are
  *       at most two queries per sequence on average and at least one
  *       (query, range) pair per compute unit; the score matrix otherwise.
  *   ws  workspace of at least sia_workspace_size(SIA_OP_INDEX_TOPK, ...) bytes

@@ -13,10 +13,12 @@ namespace sia {
 
 struct IndexArgs {
   const void* q;
-  const float* q_scale;
+  const float* q_scale;   // fp8: per token or per (token, head)
   const float* w;
   const void* k_pool;
-  const float* k_scale;
+  const float* k_scale;   // fp8: per key token
+  const uint8_t* q_mx;    // MXFP8: [T, H, 4] E8M0 group scales (groups of 32 along dim)
+  const uint8_t* k_mx;    // MXFP8: [pages, 64, 4]
   int q_scale_per_head;
   int H;
   int D;
@@ -25,8 +27,45 @@ struct IndexArgs {
   int64_t ld;
 };
 
+inline IndexArgs index_args(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld) {
+  const bool mx = in.dtype == SIA_MXFP8_E4M3;
+  return IndexArgs{in.q, mx ? nullptr : (const float*)in.q_scale, in.w, in.k_pool,
+                   mx ? nullptr : (const float*)in.k_scale, mx ? (const uint8_t*)in.q_scale : nullptr,
+                   mx ? (const uint8_t*)in.k_scale : nullptr, in.q_scale_per_head, in.heads, in.dim, s, scores, ld};
+}
+
+// Zero scale operands select the unscaled instruction (unit scales).
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Block-scaled form for MXFP8.  In this instruction the 32 bytes of a lane
+// of row (or column) m split into two K blocks of the MFMA: bytes 0..15 of
+// lanes m and m+32 form block 0, bytes 16..31 of both form block 1, and the
+// scale of block b comes from lane m + 32b (byte ST of its scale register for
+// K step ST).  The MX operands are therefore laid out so that a block is one
+// 32-element group: K step st, lane half hh holds depth [64st + 16hh, +16)
+// in bytes 0..15 and [64st + 32 + 16hh, +16) in bytes 16..31 (groups 2st and
+// 2st + 1), and lane half hh supplies the scale of group 2st + hh.
+template <int ST>
+__device__ __forceinline__ v16f mfma_mx(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, ST, (int)sa, ST, (int)sb);
+}
+
+// The scale bytes a lane supplies, from its row's four group scales (bytes
+// g0..g3 of row_word): byte st = group 2st + hh.
+__device__ __forceinline__ uint32_t mx_lane_scales(uint32_t row_word, int hh) {
+  const uint32_t w = hh ? row_word >> 8 : row_word;
+  return (w & 0xffu) | ((w >> 8) & 0xff00u);
+}
+
+// MX operand of K step ST from a 128-byte row: depth [64ST + 16hh, +16) and
+// [64ST + 32 + 16hh, +16).
+template <int ST>
+__device__ __forceinline__ v8i mx_operand(const uint8_t* row, int hh) {
+  const v4i lo = *(const v4i*)(row + 64 * ST + 16 * hh);
+  const v4i hi = *(const v4i*)(row + 64 * ST + 32 + 16 * hh);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // One wave scores query t against the 64-key pages [c_begin, c_end) of its
@@ -35,7 +74,8 @@ __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
 // Lane l: nn = l % 32 (key within an N tile / head within an M tile), hh = l / 32.
 // K-step mapping (same for both operands): step st of lane half hh covers
 // depth bytes [64*hh + 32*st, 64*hh + 32*st + 32).
-template <int HI, typename Sink>
+// MX: MXFP8 inputs (group scales inside the MFMA; no per-token scales).
+template <int HI, bool MX, typename Sink>
 __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, int b, int c_begin, int c_end,
                                             Sink&& sink) {
   constexpr int MT = HI / 32;
@@ -47,41 +87,65 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
 
   // key pages go through a ring of three register buffers: while page c is
   // computed, pages c+1 and c+2 are in flight
-  auto load_page = [&](int c, v8i (&kb)[2][2], float& ks) __attribute__((always_inline)) {
+  // ks: fp8 key scale of key 64c + lane; MX: the group-scale words of keys
+  // nn (kt = 0) and 32 + nn (kt = 1) of the page, as this lane uses them
+  struct KScale {
+    float f;
+    uint32_t w[2];
+  };
+  auto load_page = [&](int c, v8i (&kb)[2][2], KScale& ks) __attribute__((always_inline)) {
     int page = table[c];
     page = page < 0 ? 0 : (page >= a.s.num_pages ? a.s.num_pages - 1 : page);
-    const uint8_t* pb = kpool + (int64_t)page * (kPage * 128) + 64 * hh;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint8_t* kr = pb + (32 * kt + nn) * 128;
-      kb[kt][0] = *(const v8i*)(kr);
-      kb[kt][1] = *(const v8i*)(kr + 32);
+      const uint8_t* kr = kpool + (int64_t)page * (kPage * 128) + (32 * kt + nn) * 128;
+      if constexpr (MX) {
+        kb[kt][0] = mx_operand<0>(kr, hh);
+        kb[kt][1] = mx_operand<1>(kr, hh);
+      } else {
+        kb[kt][0] = *(const v8i*)(kr + 64 * hh);
+        kb[kt][1] = *(const v8i*)(kr + 64 * hh + 32);
+      }
     }
-    ks = a.k_scale[(int64_t)page * kPage + lane];
+    if constexpr (MX) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        ks.w[kt] = mx_lane_scales(*(const uint32_t*)(a.k_mx + ((int64_t)page * kPage + 32 * kt + nn) * 4), hh);
+    } else {
+      ks.f = a.k_scale[(int64_t)page * kPage + lane];
+    }
   };
   v8i k0[2][2], k1[2][2], k2[2][2];
-  float ks0 = 0.f, ks1 = 0.f, ks2 = 0.f;
+  KScale ks0{}, ks1{}, ks2{};
   load_page(c_begin, k0, ks0);
   if (c_begin + 1 < c_end) load_page(c_begin + 1, k1, ks1);
   if (c_begin + 2 < c_end) load_page(c_begin + 2, k2, ks2);
 
   // query operand (A): head m = 32*mt + nn
   v8i qa[MT][2];
+  uint32_t qsc[MT];   // MX: group scales of head 32mt + nn
   float wr[MT][16];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const uint8_t* qr = qbase + ((int64_t)t * HI + 32 * mt + nn) * 128 + 64 * hh;
-    qa[mt][0] = *(const v8i*)(qr);
-    qa[mt][1] = *(const v8i*)(qr + 32);
+    const uint8_t* qr = qbase + ((int64_t)t * HI + 32 * mt + nn) * 128;
+    if constexpr (MX) {
+      qa[mt][0] = mx_operand<0>(qr, hh);
+      qa[mt][1] = mx_operand<1>(qr, hh);
+      qsc[mt] = mx_lane_scales(*(const uint32_t*)(a.q_mx + ((int64_t)t * HI + 32 * mt + nn) * 4), hh);
+    } else {
+      qa[mt][0] = *(const v8i*)(qr + 64 * hh);
+      qa[mt][1] = *(const v8i*)(qr + 64 * hh + 32);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int head = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float qs = a.q_scale_per_head ? a.q_scale[(int64_t)t * HI + head] : a.q_scale[t];
+      float qs = 1.f;
+      if constexpr (!MX) qs = a.q_scale_per_head ? a.q_scale[(int64_t)t * HI + head] : a.q_scale[t];
       wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
     }
   }
   // scores of page c from buffer kb, then buffer kb takes page c+3
-  auto step = [&](int c, v8i (&kb)[2][2], float& ks) __attribute__((always_inline)) {
+  auto step = [&](int c, v8i (&kb)[2][2], KScale& ks) __attribute__((always_inline)) {
     float p[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -89,8 +153,13 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         v16f acc = {};
-        acc = mfma_f8(qa[mt][0], kb[kt][0], acc);
-        acc = mfma_f8(qa[mt][1], kb[kt][1], acc);
+        if constexpr (MX) {
+          acc = mfma_mx<0>(qa[mt][0], kb[kt][0], acc, qsc[mt], ks.w[kt]);
+          acc = mfma_mx<1>(qa[mt][1], kb[kt][1], acc, qsc[mt], ks.w[kt]);
+        } else {
+          acc = mfma_f8(qa[mt][0], kb[kt][0], acc);
+          acc = mfma_f8(qa[mt][1], kb[kt][1], acc);
+        }
         // ReLU as an integer max: negative floats (and -0) have the sign bit
         // set, so max(bits, 0) is 0 for them and the identity otherwise (one
         // instruction; fmaxf would also quiet NaNs first)
@@ -103,7 +172,8 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
     // lane 32+l the other half: swap the cross halves, then one add gives lane
     // l the score of key 64*c + l
     const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
-    float score = (__uint_as_float(hv[0]) + __uint_as_float(hv[1])) * ks;
+    float score = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
+    if constexpr (!MX) score *= ks.f;
     const int s = c * 64 + lane;
     if (s > pos) score = -INFINITY;
     sink(s, score);

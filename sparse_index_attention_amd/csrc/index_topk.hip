@@ -42,7 +42,7 @@ struct RangeSmem {
   uint32_t found_bin, found_above;
 };
 
-template <int HI>
+template <int HI, bool MX>
 __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int K, int n_ranges,
                                                                float* __restrict__ cscore,
                                                                int32_t* __restrict__ cpos, int64_t ldc) {
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
     const int cb = c0 + 16 * w;
     const int ce = cb + 16 < c1 ? cb + 16 : c1;
     if (cb < ce)
-      score_pages<HI>(a, t, pos, b, cb, ce, [&](int s, float score) __attribute__((always_inline)) {
+      score_pages<HI, MX>(a, t, pos, b, cb, ce, [&](int s, float score) __attribute__((always_inline)) {
         sh.sc[s - key0] = score;
       });
   }
@@ -190,15 +190,23 @@ int64_t index_topk_ld(int max_visible, int K) {
 hipError_t launch_index_topk(const sia_indexer_in& in, const SeqArgs& s, int K, int order, int32_t* idx,
                              float* vals, float* cscore, int32_t* cpos, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  IndexArgs a{in.q, in.q_scale, in.w, in.k_pool, in.k_scale, in.q_scale_per_head, in.heads, in.dim, s, nullptr, 0};
+  const IndexArgs a = index_args(in, s, nullptr, 0);
+  const bool mx = in.dtype == SIA_MXFP8_E4M3;
   const int n_ranges = index_topk_ranges(s.max_visible);
   const int64_t ldc = index_topk_ld(s.max_visible, K);
   if (n_ranges > 0) {
     const dim3 grid((unsigned)((int64_t)s.T * n_ranges));
-    if (in.heads == 64)
-      hipLaunchKernelGGL(k_index_topk_ranges<64>, grid, dim3(kRNT), 0, st, a, K, n_ranges, cscore, cpos, ldc);
-    else
-      hipLaunchKernelGGL(k_index_topk_ranges<32>, grid, dim3(kRNT), 0, st, a, K, n_ranges, cscore, cpos, ldc);
+    if (in.heads == 64) {
+      if (mx)
+        hipLaunchKernelGGL((k_index_topk_ranges<64, true>), grid, dim3(kRNT), 0, st, a, K, n_ranges, cscore, cpos, ldc);
+      else
+        hipLaunchKernelGGL((k_index_topk_ranges<64, false>), grid, dim3(kRNT), 0, st, a, K, n_ranges, cscore, cpos, ldc);
+    } else {
+      if (mx)
+        hipLaunchKernelGGL((k_index_topk_ranges<32, true>), grid, dim3(kRNT), 0, st, a, K, n_ranges, cscore, cpos, ldc);
+      else
+        hipLaunchKernelGGL((k_index_topk_ranges<32, false>), grid, dim3(kRNT), 0, st, a, K, n_ranges, cscore, cpos, ldc);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

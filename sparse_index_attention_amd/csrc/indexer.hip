@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_index_scores_f32(IndexArgs a) {
 // Lane l: nn = l % 32 (key within an N tile / head within an M tile), hh = l / 32.
 // K-step mapping (same for both operands): step st of lane half hh covers
 // depth bytes [64*hh + 32*st, 64*hh + 32*st + 32).
-template <int HI>
+template <int HI, bool MX>
 __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_qblocks, int n_chunks,
                                                              int chunks_per_item) {
   const int wave = threadIdx.x >> 6;
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
     if (c_begin >= c_end) continue;
 
     float* srow = a.scores + (int64_t)t * a.ld;
-    score_pages<HI>(a, t, pos, b, c_begin, c_end, [&](int s, float score) __attribute__((always_inline)) {
+    score_pages<HI, MX>(a, t, pos, b, c_begin, c_end, [&](int s, float score) __attribute__((always_inline)) {
       if (s < a.s.max_visible) srow[s] = score;
     });
   }
@@ -114,7 +114,7 @@ struct KStage {  // one thread's share of a key page in flight: 32 bytes and a s
   float s;
 };
 
-template <int HI>
+template <int HI, bool MX>
 __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexArgs a, int n_qblocks) {
   constexpr int MT = HI / 32;
   __shared__ __attribute__((aligned(16))) uint8_t kl[2][kPage * 128];
@@ -150,18 +150,26 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
 
   // ---- this wave's query (operand A) and folded head weights
   v8i qa[MT][2];
+  uint32_t qsc[MT];   // MX: group scales of head 32mt + nn
   float wr[MT][16];
   if (has_q) {
     const uint8_t* __restrict__ qbase = (const uint8_t*)a.q;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint8_t* qr = qbase + ((int64_t)t * HI + 32 * mt + nn) * 128 + 64 * hh;
-      qa[mt][0] = *(const v8i*)(qr);
-      qa[mt][1] = *(const v8i*)(qr + 32);
+      const uint8_t* qr = qbase + ((int64_t)t * HI + 32 * mt + nn) * 128;
+      if constexpr (MX) {
+        qa[mt][0] = mx_operand<0>(qr, hh);
+        qa[mt][1] = mx_operand<1>(qr, hh);
+        qsc[mt] = mx_lane_scales(*(const uint32_t*)(a.q_mx + ((int64_t)t * HI + 32 * mt + nn) * 4), hh);
+      } else {
+        qa[mt][0] = *(const v8i*)(qr + 64 * hh);
+        qa[mt][1] = *(const v8i*)(qr + 64 * hh + 32);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int head = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const float qs = a.q_scale_per_head ? a.q_scale[(int64_t)t * HI + head] : a.q_scale[t];
+        float qs = 1.f;
+        if constexpr (!MX) qs = a.q_scale_per_head ? a.q_scale[(int64_t)t * HI + head] : a.q_scale[t];
         wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
       }
     }
@@ -175,13 +183,22 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
       const int r = 32 * kt + nn;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int j0 = 4 * hh + 2 * st;
+        // 16-byte chunks of the row this lane feeds (see mx_operand for MX)
+        const int j0 = MX ? 4 * st + hh : 4 * hh + 2 * st;
+        const int j1 = MX ? 4 * st + 2 + hh : 4 * hh + 2 * st + 1;
         const uint4 lo = *(const uint4*)&kl[cur][kswz(r, j0)];
-        const uint4 hi = *(const uint4*)&kl[cur][kswz(r, j0 + 1)];
+        const uint4 hi = *(const uint4*)&kl[cur][kswz(r, j1)];
         kb[kt][st] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
+    // fp8: key scale of key `lane`; MX: the staged words hold each key's four
+    // group-scale bytes
     const float ks = kls[cur][lane];
+    uint32_t ksc[2] = {0u, 0u};
+    if constexpr (MX) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) ksc[kt] = mx_lane_scales(__float_as_uint(kls[cur][32 * kt + nn]), hh);
+    }
     float p[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -189,8 +206,13 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         v16f acc = {};
-        acc = mfma_f8(qa[mt][0], kb[kt][0], acc);
-        acc = mfma_f8(qa[mt][1], kb[kt][1], acc);
+        if constexpr (MX) {
+          acc = mfma_mx<0>(qa[mt][0], kb[kt][0], acc, qsc[mt], ksc[kt]);
+          acc = mfma_mx<1>(qa[mt][1], kb[kt][1], acc, qsc[mt], ksc[kt]);
+        } else {
+          acc = mfma_f8(qa[mt][0], kb[kt][0], acc);
+          acc = mfma_f8(qa[mt][1], kb[kt][1], acc);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sum = fmaf(wr[mt][r], __int_as_float(max(__float_as_int(acc[r]), 0)), sum);
       }
@@ -200,7 +222,8 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
     // lane 32+l the other half: swap the cross halves, then one add gives lane
     // l the score of key l
     const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
-    float score = (__uint_as_float(hv[0]) + __uint_as_float(hv[1])) * ks;
+    float score = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
+    if constexpr (!MX) score *= ks;
     if (c * 64 + 63 > pos) score = c * 64 + lane > pos ? -INFINITY : score;
     // the row's buffer ends at max_visible: the range check on the vector
     // offset drops stores past it
@@ -241,7 +264,12 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
       KStage g;
       g.x = *(const uint4*)src;
       g.y = *(const uint4*)(src + 16);
-      g.s = a.k_scale[(int64_t)page * kPage + lane];  // every wave loads it, wave 0 stores it
+      // every wave loads it, wave 0 stores it: fp8 the key scale, MX the key's
+      // four group-scale bytes (as raw bits)
+      if constexpr (MX)
+        g.s = __uint_as_float(*(const uint32_t*)(a.k_mx + ((int64_t)page * kPage + lane) * 4));
+      else
+        g.s = a.k_scale[(int64_t)page * kPage + lane];
       return g;
     };
     auto lwrite = [&](int buf, const KStage& g) __attribute__((always_inline)) {
@@ -275,8 +303,9 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
 
 hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,
                                hipStream_t st) {
-  IndexArgs a{in.q, in.q_scale, in.w, in.k_pool, in.k_scale, in.q_scale_per_head, in.heads, in.dim, s, scores, ld};
+  const IndexArgs a = index_args(in, s, scores, ld);
   if (s.T == 0 || s.max_visible == 0) return hipSuccess;
+  const bool mx = in.dtype == SIA_MXFP8_E4M3;
   if (in.dtype == SIA_F32) {
     dim3 grid(s.T, (s.max_visible + 255) / 256);
     hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(256), 0, st, a);
@@ -288,10 +317,18 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
     const int nqb = (s.T + kSQ - 1) / kSQ;
     const int64_t grid = (int64_t)nqb * ((n_chunks + kSChunk - 1) / kSChunk);
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (in.heads == 64)
-      hipLaunchKernelGGL(k_index_scores_fp8_shared<64>, dim3((unsigned)grid), dim3(kSThreads), 0, st, a, nqb);
-    else
-      hipLaunchKernelGGL(k_index_scores_fp8_shared<32>, dim3((unsigned)grid), dim3(kSThreads), 0, st, a, nqb);
+    const dim3 g((unsigned)grid), blk(kSThreads);
+    if (in.heads == 64) {
+      if (mx)
+        hipLaunchKernelGGL((k_index_scores_fp8_shared<64, true>), g, blk, 0, st, a, nqb);
+      else
+        hipLaunchKernelGGL((k_index_scores_fp8_shared<64, false>), g, blk, 0, st, a, nqb);
+    } else {
+      if (mx)
+        hipLaunchKernelGGL((k_index_scores_fp8_shared<32, true>), g, blk, 0, st, a, nqb);
+      else
+        hipLaunchKernelGGL((k_index_scores_fp8_shared<32, false>), g, blk, 0, st, a, nqb);
+    }
     return hipGetLastError();
   }
   const int n_qblocks = (s.T + 3) / 4;
@@ -305,10 +342,17 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
   const int64_t items = (int64_t)n_qblocks * ((n_chunks + cpi - 1) / cpi);
   const int64_t resident = (int64_t)cus * 2;
   const int grid = (int)(items < resident ? items : resident);
-  if (in.heads == 64)
-    hipLaunchKernelGGL(k_index_scores_fp8<64>, dim3(grid), dim3(256), 0, st, a, n_qblocks, n_chunks, cpi);
-  else
-    hipLaunchKernelGGL(k_index_scores_fp8<32>, dim3(grid), dim3(256), 0, st, a, n_qblocks, n_chunks, cpi);
+  if (in.heads == 64) {
+    if (mx)
+      hipLaunchKernelGGL((k_index_scores_fp8<64, true>), dim3(grid), dim3(256), 0, st, a, n_qblocks, n_chunks, cpi);
+    else
+      hipLaunchKernelGGL((k_index_scores_fp8<64, false>), dim3(grid), dim3(256), 0, st, a, n_qblocks, n_chunks, cpi);
+  } else {
+    if (mx)
+      hipLaunchKernelGGL((k_index_scores_fp8<32, true>), dim3(grid), dim3(256), 0, st, a, n_qblocks, n_chunks, cpi);
+    else
+      hipLaunchKernelGGL((k_index_scores_fp8<32, false>), dim3(grid), dim3(256), 0, st, a, n_qblocks, n_chunks, cpi);
+  }
   return hipGetLastError();
 }
 

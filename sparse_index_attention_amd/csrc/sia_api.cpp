@@ -44,10 +44,13 @@ static int check_indexer(const sia_indexer_in* in) {
   if (in->heads < 1 || in->dim < 1) return SIA_ERR_INVALID_ARG;
   if (in->dtype == SIA_F32) {
     if (in->heads > 64 || (int64_t)in->heads * in->dim > 4096) return SIA_ERR_UNSUPPORTED;
-  } else if (in->dtype == SIA_FP8_E4M3) {
+  } else if (in->dtype == SIA_FP8_E4M3 || in->dtype == SIA_MXFP8_E4M3) {
     if (!in->q_scale || !in->k_scale) return SIA_ERR_INVALID_ARG;
     if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
     if (!aligned16(in->q) || !aligned16(in->k_pool)) return SIA_ERR_INVALID_ARG;
+    if (in->dtype == SIA_MXFP8_E4M3 &&
+        ((reinterpret_cast<uintptr_t>(in->q_scale) & 3u) || (reinterpret_cast<uintptr_t>(in->k_scale) & 3u)))
+      return SIA_ERR_INVALID_ARG;
   } else {
     return SIA_ERR_UNSUPPORTED;
   }
@@ -109,7 +112,7 @@ using namespace sia;
 // decode-like batches (few queries per sequence) large enough to give every
 // compute unit a (query, range) workgroup.
 static int index_topk_auto(const sia_indexer_in& in, const sia_seqmap& seq) {
-  if (in.dtype != SIA_FP8_E4M3) return SIA_INDEX_TOPK_SCORES;
+  if (in.dtype != SIA_FP8_E4M3 && in.dtype != SIA_MXFP8_E4M3) return SIA_INDEX_TOPK_SCORES;
   const int64_t wgs = (int64_t)seq.num_tokens * index_topk_ranges(seq.max_visible);
   return seq.num_tokens <= 2 * seq.batch && wgs >= num_cus() ? SIA_INDEX_TOPK_ONCHIP : SIA_INDEX_TOPK_SCORES;
 }
@@ -236,7 +239,8 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
   if (K < 1 || (order != 0 && order != 1) || !idx) return SIA_ERR_INVALID_ARG;
   if (method < SIA_INDEX_TOPK_AUTO || method > SIA_INDEX_TOPK_SCORES) return SIA_ERR_INVALID_ARG;
   if (K > 2048) return SIA_ERR_UNSUPPORTED;
-  if (method == SIA_INDEX_TOPK_ONCHIP && in->dtype != SIA_FP8_E4M3) return SIA_ERR_UNSUPPORTED;
+  if (method == SIA_INDEX_TOPK_ONCHIP && in->dtype != SIA_FP8_E4M3 && in->dtype != SIA_MXFP8_E4M3)
+    return SIA_ERR_UNSUPPORTED;
   if (seq->num_tokens == 0) return SIA_OK;
   const size_t need = sia_workspace_size(SIA_OP_INDEX_TOPK, seq, K, 1, 1);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;

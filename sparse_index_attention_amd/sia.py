@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsia.so")
 _lib = None
 
-SIA_F32, SIA_BF16, SIA_FP8_E4M3 = 0, 1, 2
+SIA_F32, SIA_BF16, SIA_FP8_E4M3, SIA_MXFP8_E4M3 = 0, 1, 2, 3
 OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_INDEX_SELECT_ATTEND, OP_INDEX_TOPK = 0, 1, 2, 3, 4
 INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP, INDEX_TOPK_SCORES = 0, 1, 2
 
@@ -140,16 +140,21 @@ class SeqMap:
 
 @dataclass
 class Indexer:
-    q: torch.Tensor              # [T, Hi, Di] uint8 (e4m3 codes) or float32
+    """q, k_pool: uint8 e4m3 codes or float32.  fp8: q_scale [T] or [T, Hi] and
+    k_scale [P, 64] float32.  MXFP8: q_scale [T, Hi, Di/32] and k_scale
+    [P, 64, Di/32] uint8 E8M0 group scales (a uint8 q_scale selects MXFP8)."""
+    q: torch.Tensor              # [T, Hi, Di]
     w: torch.Tensor              # [T, Hi] float32
     k_pool: torch.Tensor         # [P, 64, Di] same dtype as q
-    q_scale: torch.Tensor = None  # [T] or [T, Hi] float32 (fp8)
-    k_scale: torch.Tensor = None  # [P, 64] float32 (fp8)
+    q_scale: torch.Tensor = None
+    k_scale: torch.Tensor = None
 
     def c(self) -> IndexerC:
-        per_head = int(self.q_scale is not None and self.q_scale.dim() == 2)
+        mx = self.q_scale is not None and self.q_scale.dtype == torch.uint8
+        per_head = int(not mx and self.q_scale is not None and self.q_scale.dim() == 2)
+        code = SIA_MXFP8_E4M3 if mx else dtype_code(self.q)
         return IndexerC(_ptr(self.q), _ptr(self.q_scale), _ptr(self.w), _ptr(self.k_pool), _ptr(self.k_scale),
-                        dtype_code(self.q), per_head, self.q.shape[1], self.q.shape[2])
+                        code, per_head, self.q.shape[1], self.q.shape[2])
 
 
 @dataclass

@@ -95,6 +95,9 @@ def test_seqmap_validation(Lcpu, kw, code):
     (dict(dtype=7), -2),
     (dict(q=FAKE + 4), -1),               # misaligned fp8 operand
     (dict(dtype=sia.SIA_F32, heads=65, dim=4), -2),
+    (dict(dtype=sia.SIA_MXFP8_E4M3, q_scale=FAKE + 2), -1),   # E8M0 scales need 4-byte alignment
+    (dict(dtype=sia.SIA_MXFP8_E4M3, k_scale=FAKE + 1), -1),
+    (dict(dtype=sia.SIA_MXFP8_E4M3, heads=16), -2),
 ])
 def test_indexer_validation(Lcpu, kw, code):
     L = Lcpu

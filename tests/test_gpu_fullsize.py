@@ -21,7 +21,7 @@ from gpu_support import check_attention, check_scores, dev, kind_of, tie_band_ok
 pytestmark = pytest.mark.gpu
 
 # name -> number of sampled query rows
-CASES = {"decode": 6, "quant_decode": 3, "long_prefill": 10, "cp_chunk_prefill": 8}
+CASES = {"decode": 6, "quant_decode": 3, "long_prefill": 10, "cp_chunk_prefill": 8, "mx_decode": 3}
 
 
 @pytest.fixture(scope="module", autouse=True)

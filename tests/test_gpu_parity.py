@@ -17,7 +17,7 @@ from gpu_support import (check_attention, check_scores, dev, kind_of, tie_band_o
 pytestmark = pytest.mark.gpu
 
 TINY = ["tiny_prefill", "decode_tiny", "prefill_tiny", "quant_decode_tiny", "quant_decode_tile128_tiny",
-        "cp_chunk_prefill_tiny", "decode_h64_tiny", "chunked_prefill_tiny"]
+        "cp_chunk_prefill_tiny", "decode_h64_tiny", "chunked_prefill_tiny", "mx_decode_tiny", "mx_prefill_tiny"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -309,7 +309,7 @@ def test_index_topk_matches_scores_then_topk(name, order):
     seq, ix, _, _ = upload(wl)
     _, e_idx, e_vals = _unfused_topk(ix, seq, K, order)
     methods = [sia.INDEX_TOPK_AUTO, sia.INDEX_TOPK_SCORES]
-    if wl.cfg["idx_dtype"] == "fp8":
+    if wl.cfg["idx_dtype"] in ("fp8", "mxfp8"):
         methods.append(sia.INDEX_TOPK_ONCHIP)
     for m in methods:
         g_idx, g_vals = sia.index_topk(ix, seq, K, order=order, method=m, with_vals=True)
