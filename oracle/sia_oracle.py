@@ -36,7 +36,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "decode_e4m3", "decode_bf16", "decode_e8m0", "mx_values", "physical_slots", "key_rows", "kv_rows",
+    "decode_e4m3", "decode_bf16", "decode_e8m0", "mx_values", "encode_e4m3", "quantize_q_fp8", "quantize_q_mx",
+    "physical_slots", "key_rows", "kv_rows",
     "index_scores_row", "index_scores", "topk_row", "topk", "sparse_mla_row",
     "sparse_mla", "merge_partials", "index_select_attend",
 ]
@@ -85,6 +86,63 @@ def mx_values(codes, scales, group=32) -> np.ndarray:
     v = decode_e4m3(codes)
     sc = decode_e8m0(scales)
     return v * np.repeat(sc, group, axis=-1)
+
+
+_E4M3_GRID = None
+
+
+def encode_e4m3(v) -> np.ndarray:
+    """float -> e4m3 code: the nearest value of the format's grid (ties to the
+    even code), saturating to +-448, sign kept (so -0 -> 0x80).  The grid is
+    the decoded value of every finite code 0x00..0x7e."""
+    global _E4M3_GRID
+    if _E4M3_GRID is None:
+        _E4M3_GRID = decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    x = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_GRID, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_GRID[lo], _E4M3_GRID[hi] - a
+    code = np.where((dhi < dlo) | ((dhi == dlo) & ((hi & 1) == 0)), hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+
+
+def quantize_q_fp8(q_bits):
+    """Dynamic per-token fp8 quantization of bf16 queries [T, Hi, Di] -> (e4m3
+    codes, float32 scale [T]).
+
+    The indexer prolog quantizes Q on the fly ([P2, section 3.2 "Q
+    quantization"]; [P3, section 2, three-stream prolog]).  Reading: one scale
+    per token from its absolute maximum, scale = amax / 448 and codes =
+    e4m3(x * (448 / amax)), both divisions and the product in float32 (a token
+    of zeros gets scale 1 and zero codes)."""
+    x = decode_bf16(q_bits).astype(np.float32)
+    T = x.shape[0]
+    amax = np.max(np.abs(x.reshape(T, -1)), axis=1).astype(np.float32)
+    nz = amax > 0
+    r = np.where(nz, np.float32(448.0) / np.where(nz, amax, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    scale = np.where(nz, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = (x * r.reshape((T,) + (1,) * (x.ndim - 1))).astype(np.float32)
+    return encode_e4m3(v), scale
+
+
+def quantize_q_mx(q_bits, group=32):
+    """Dynamic MXFP8 quantization of bf16 queries [T, Hi, Di] -> (e4m3 codes,
+    E8M0 bytes [T, Hi, Di/group]).
+
+    MXFP8 groups of 32 with a shared power-of-two scale ([P2, section 4.1];
+    [P5, section 4 table]).  Reading: the scale is the smallest 2^e with
+    amax <= 448 * 2^e (no element saturates; with amax = m * 2^E, m in
+    [0.5, 1): e = E - 9 if m <= 0.875 else E - 8), byte e + 127, and an
+    all-zero group gets byte 0; codes = e4m3(x * 2^-e)."""
+    x = decode_bf16(q_bits)
+    g = x.reshape(*x.shape[:-1], x.shape[-1] // group, group)
+    amax = np.max(np.abs(g), axis=-1)
+    m, E = np.frexp(amax)
+    e = np.where(m <= 0.875, E - 9, E - 8)
+    e = np.clip(np.where(amax > 0, e, -127), -127, 127).astype(np.int64)
+    codes = encode_e4m3(g * np.ldexp(1.0, -e)[..., None]).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
 
 
 def decode_bf16(bits) -> np.ndarray:

@@ -232,6 +232,55 @@ def test_mx_generator_roundtrip():
     assert np.all(amax <= 448 * s) and np.all(amax > 224 * s)   # the smallest power of two that fits
 
 
+def test_encode_e4m3_grid_ties_and_saturation():
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    assert np.array_equal(O.encode_e4m3(O.decode_e4m3(finite)), finite)        # every value maps to its code
+    # midpoints between neighbours round to the even code
+    for c in range(0x00, 0x7E):
+        mid = (O.decode_e4m3(np.uint8(c)) + O.decode_e4m3(np.uint8(c + 1))) / 2
+        assert O.encode_e4m3(mid) == (c if c % 2 == 0 else c + 1), c
+    assert O.encode_e4m3(1e6) == 0x7E and O.encode_e4m3(-500.0) == 0xFE and O.encode_e4m3(460.0) == 0x7E
+    assert O.encode_e4m3(2.0 ** -11) == 0x00 and O.encode_e4m3(-0.0) == 0x80
+
+
+def _bf16_bits(x):
+    return W.to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_quantize_q_fp8_per_token():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((5, 4, 32)).astype(np.float32) * np.array([1, 10, 0.01, 1e-3, 0])[:, None, None]
+    bits = _bf16_bits(x)
+    codes, scale = O.quantize_q_fp8(bits)
+    xv = O.decode_bf16(bits)
+    for t in range(4):
+        amax = np.max(np.abs(xv[t]))
+        assert scale[t] == np.float32(np.float32(amax) / np.float32(448))
+        back = O.decode_e4m3(codes[t]) * scale[t]
+        assert np.max(np.abs(O.decode_e4m3(codes[t]))) == 448.0                  # the extreme element hits the top
+        assert np.all(np.abs(back - xv[t]) <= np.abs(xv[t]) * 2.0 ** -4 + scale[t] * 2.0 ** -10 + 1e-30)
+    assert scale[4] == 1.0 and np.all(O.decode_e4m3(codes[4]) == 0)
+
+
+def test_quantize_q_mx_scale_rule_brute_force():
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((3, 2, 64)) * 10.0 ** rng.integers(-6, 6, size=(3, 2, 1))).astype(np.float32)
+    x[2, 1, 32:] = 0.0
+    bits = _bf16_bits(x)
+    codes, e8 = O.quantize_q_mx(bits)
+    xv = O.decode_bf16(bits).reshape(3, 2, 2, 32)
+    for idx in np.ndindex(3, 2, 2):
+        amax = np.max(np.abs(xv[idx]))
+        if amax == 0:
+            assert e8[idx] == 0
+            continue
+        e = next(k for k in range(-140, 140) if amax <= 448 * 2.0 ** k)   # smallest fitting power of two
+        assert int(e8[idx]) == e + 127
+        c = codes.reshape(3, 2, 2, 32)[idx]
+        assert np.array_equal(c, O.encode_e4m3(xv[idx] * 2.0 ** -e))
+
+
 # ---------------------------------------------------------------------------
 # Top-K
 # ---------------------------------------------------------------------------
