@@ -84,7 +84,9 @@ typedef struct {
 
 /* Indexer inputs [P1, "Sparse Attention Pipeline Optimization"; P2, section 3.1].
  *   q        [T, heads, dim]  e4m3 codes (SIA_FP8_E4M3, SIA_MXFP8_E4M3) or
- *            float (SIA_F32)
+ *            float (SIA_F32); with q_bf16 = 1, bfloat16 queries that are
+ *            quantized on the fly to the indexer's format (see
+ *            sia_quantize_indexer_q); q_scale is then unused
  *   q_scale  SIA_FP8_E4M3: float [T] (q_scale_per_head = 0) or [T, heads] (= 1)
  *            SIA_MXFP8_E4M3: uint8 [T, heads, dim/32], one OCP E8M0 scale
  *            (2^(e-127)) per 32 consecutive elements of a head's q [P1,
@@ -107,6 +109,7 @@ typedef struct {
   int32_t q_scale_per_head;
   int32_t heads;
   int32_t dim;
+  int32_t q_bf16;  /* 1: q holds bfloat16 values to quantize (fp8 / MXFP8 indexers only) */
 } sia_indexer_in;
 
 /* Latent KV cache [P1, "Hierarchical Quantization"; P5, section 4 table].
@@ -183,6 +186,25 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
 /* The method SIA_INDEX_TOPK_AUTO picks for these arguments (host-side only; a
  * negative status for arguments sia_index_topk would reject).                 */
 int sia_index_topk_method(const sia_indexer_in* in, const sia_seqmap* seq);
+
+/* Dynamic Q quantization — the weight-free step of the indexer prolog [P2,
+ * section 3.2 (Q quantization on the decode critical path); P2, section 4.1 and
+ * P5, section 4 table (MXFP8 groups of 32)].  in->q holds bfloat16 queries
+ * [T, heads, dim] (in->q_bf16 = 1); the result is what sia_index_scores takes
+ * for in->dtype:
+ *   SIA_FP8_E4M3: q_codes [T, heads, dim] e4m3, q_scales float [T]:
+ *       scale = amax / 448 over the token, codes = e4m3(x * (448 / amax))
+ *       (fp32, round to nearest even; a token of zeros: scale 1, zero codes)
+ *   SIA_MXFP8_E4M3: q_codes as above, q_scales uint8 [T, heads, dim/32]: per
+ *       32 elements the smallest 2^e with amax <= 448 * 2^e (E8M0 byte e+127,
+ *       0 for an all-zero group), codes = e4m3(x * 2^-e)
+ * e4m3 rounding is to the nearest value, ties to the even code, saturating at
+ * 448.  q_codes 16-byte aligned, q_scales 4-byte aligned.  sia_index_topk and
+ * sia_index_select_attend run this step themselves (into their workspace) when
+ * in->q_bf16 = 1; sia_index_scores requires quantized input (else
+ * SIA_ERR_UNSUPPORTED).                                                       */
+int sia_quantize_indexer_q(const sia_indexer_in* in, int32_t num_tokens, void* q_codes, void* q_scales,
+                           hipStream_t stream);
 
 /* Step 3 — sparse MLA attention over the selected rows [P1, "Sparse Attention
  * Pipeline Optimization"; P3, section 3.2].  For each token t and head h, over

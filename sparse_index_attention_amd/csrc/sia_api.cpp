@@ -42,14 +42,17 @@ static int check_seq(const sia_seqmap* s) {
 static int check_indexer(const sia_indexer_in* in) {
   if (!in || !in->q || !in->w || !in->k_pool) return SIA_ERR_INVALID_ARG;
   if (in->heads < 1 || in->dim < 1) return SIA_ERR_INVALID_ARG;
+  if (in->q_bf16 != 0 && in->q_bf16 != 1) return SIA_ERR_INVALID_ARG;
   if (in->dtype == SIA_F32) {
+    if (in->q_bf16) return SIA_ERR_UNSUPPORTED;
     if (in->heads > 64 || (int64_t)in->heads * in->dim > 4096) return SIA_ERR_UNSUPPORTED;
   } else if (in->dtype == SIA_FP8_E4M3 || in->dtype == SIA_MXFP8_E4M3) {
-    if (!in->q_scale || !in->k_scale) return SIA_ERR_INVALID_ARG;
+    if ((!in->q_bf16 && !in->q_scale) || !in->k_scale) return SIA_ERR_INVALID_ARG;
     if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
     if (!aligned16(in->q) || !aligned16(in->k_pool)) return SIA_ERR_INVALID_ARG;
     if (in->dtype == SIA_MXFP8_E4M3 &&
-        ((reinterpret_cast<uintptr_t>(in->q_scale) & 3u) || (reinterpret_cast<uintptr_t>(in->k_scale) & 3u)))
+        ((!in->q_bf16 && (reinterpret_cast<uintptr_t>(in->q_scale) & 3u)) ||
+         (reinterpret_cast<uintptr_t>(in->k_scale) & 3u)))
       return SIA_ERR_INVALID_ARG;
   } else {
     return SIA_ERR_UNSUPPORTED;
@@ -118,15 +121,41 @@ static int index_topk_auto(const sia_indexer_in& in, const sia_seqmap& seq) {
 }
 
 // Workspace of either method: candidate lists (scores, positions) or the score matrix.
+// Workspace of either method: quantized queries (used when the caller passes
+// bf16 queries; sized for the largest supported indexer, 64 heads x 128), then
+// candidate lists (scores, positions) or the score matrix.
+constexpr size_t kQCodesPerToken = 64 * 128, kQScalesPerToken = 64 * 4;
+static size_t q_ws_bytes(const sia_seqmap& seq) {
+  return align256((size_t)seq.num_tokens * kQCodesPerToken) + align256((size_t)seq.num_tokens * kQScalesPerToken);
+}
 static size_t index_topk_ws_bytes(const sia_seqmap& seq, int K) {
   const size_t cand = (size_t)seq.num_tokens * index_topk_ld(seq.max_visible, K);
   const size_t onchip = 2 * align256(cand * sizeof(float));
   const size_t matrix = align256((size_t)seq.num_tokens * fused_ld(&seq) * sizeof(float));
-  return onchip > matrix ? onchip : matrix;
+  return q_ws_bytes(seq) + (onchip > matrix ? onchip : matrix);
 }
 
-static hipError_t run_index_topk(int method, const sia_indexer_in& in, const sia_seqmap& seq, int K, int order,
-                                 int32_t* idx, float* vals, void* ws, hipStream_t stream) {
+// With bf16 queries: quantize them into the workspace and describe the result
+// in `out` (the caller's struct with q, q_scale pointing at the workspace).
+static hipError_t prepare_q(const sia_indexer_in& in, const sia_seqmap& seq, void* ws, sia_indexer_in& out,
+                            hipStream_t stream) {
+  out = in;
+  if (!in.q_bf16) return hipSuccess;
+  unsigned char* codes = static_cast<unsigned char*>(ws);
+  unsigned char* scales = codes + align256((size_t)seq.num_tokens * kQCodesPerToken);
+  out.q = codes;
+  out.q_scale = scales;
+  out.q_scale_per_head = 0;
+  out.q_bf16 = 0;
+  return launch_quantize_q(in.q, seq.num_tokens, in.heads, in.dim, in.dtype == SIA_MXFP8_E4M3, codes, scales, stream);
+}
+
+static hipError_t run_index_topk(int method, const sia_indexer_in& in_given, const sia_seqmap& seq, int K,
+                                 int order, int32_t* idx, float* vals, void* ws_all, hipStream_t stream) {
+  sia_indexer_in in;
+  hipError_t eq = prepare_q(in_given, seq, ws_all, in, stream);
+  if (eq != hipSuccess) return eq;
+  void* ws = static_cast<unsigned char*>(ws_all) + q_ws_bytes(seq);
   const SeqArgs s = seq_args(seq);
   if (method == SIA_INDEX_TOPK_ONCHIP) {
     const size_t cand = (size_t)seq.num_tokens * index_topk_ld(seq.max_visible, K);
@@ -164,6 +193,7 @@ int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* sco
   if (rc) return rc;
   rc = check_scores(scores, ld, seq);
   if (rc) return rc;
+  if (in->q_bf16) return SIA_ERR_UNSUPPORTED;   // quantize first (sia_quantize_indexer_q)
   const hipError_t e = launch_index_scores(*in, seq_args(*seq), scores, ld, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);
 }
@@ -246,6 +276,18 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
   if (method == SIA_INDEX_TOPK_AUTO) method = index_topk_auto(*in, *seq);
   const hipError_t e = run_index_topk(method, *in, *seq, K, order, idx, vals, ws, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+int sia_quantize_indexer_q(const sia_indexer_in* in, int32_t num_tokens, void* q_codes, void* q_scales,
+                           hipStream_t stream) {
+  if (!in || !in->q || in->q_bf16 != 1 || num_tokens < 0 || !q_codes || !q_scales) return SIA_ERR_INVALID_ARG;
+  if (in->dtype != SIA_FP8_E4M3 && in->dtype != SIA_MXFP8_E4M3) return SIA_ERR_UNSUPPORTED;
+  if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
+  if (!aligned16(in->q) || !aligned16(q_codes) || (reinterpret_cast<uintptr_t>(q_scales) & 3u))
+    return SIA_ERR_INVALID_ARG;
+  const hipError_t e = launch_quantize_q(in->q, num_tokens, in->heads, in->dim, in->dtype == SIA_MXFP8_E4M3,
+                                         static_cast<uint8_t*>(q_codes), q_scales, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);
 }
 

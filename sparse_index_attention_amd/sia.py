@@ -31,7 +31,8 @@ class SeqMapC(ctypes.Structure):
 
 class IndexerC(ctypes.Structure):
     _fields_ = [("q", c_p), ("q_scale", c_p), ("w", c_p), ("k_pool", c_p), ("k_scale", c_p),
-                ("dtype", ctypes.c_int), ("q_scale_per_head", c_i32), ("heads", c_i32), ("dim", c_i32)]
+                ("dtype", ctypes.c_int), ("q_scale_per_head", c_i32), ("heads", c_i32), ("dim", c_i32),
+                ("q_bf16", c_i32)]
 
 
 class KvC(ctypes.Structure):
@@ -58,6 +59,7 @@ def lib():
         L.sia_index_scores.argtypes = [P(IndexerC), P(SeqMapC), c_p, c_i64, c_p]
         L.sia_topk.argtypes = [c_p, c_i64, P(SeqMapC), c_i32, c_i32, c_p, c_p, c_p]
         L.sia_index_topk_method.argtypes = [P(IndexerC), P(SeqMapC)]
+        L.sia_quantize_indexer_q.argtypes = [P(IndexerC), c_i32, c_p, c_p, c_p]
         L.sia_index_topk.argtypes = [P(IndexerC), P(SeqMapC), c_i32, c_i32, c_i32, c_p, c_p, c_p, ctypes.c_size_t,
                                      c_p]
         mla = [c_p, ctypes.c_int, c_i32, P(KvC), P(SeqMapC), c_p, c_i32, ctypes.c_float, c_p, c_p, c_p,
@@ -142,7 +144,8 @@ class SeqMap:
 class Indexer:
     """q, k_pool: uint8 e4m3 codes or float32.  fp8: q_scale [T] or [T, Hi] and
     k_scale [P, 64] float32.  MXFP8: q_scale [T, Hi, Di/32] and k_scale
-    [P, 64, Di/32] uint8 E8M0 group scales (a uint8 q_scale selects MXFP8)."""
+    [P, 64, Di/32] uint8 E8M0 group scales (uint8 scales select MXFP8).  A
+    bfloat16 q with e4m3 keys is quantized on the fly (q_scale unused)."""
     q: torch.Tensor              # [T, Hi, Di]
     w: torch.Tensor              # [T, Hi] float32
     k_pool: torch.Tensor         # [P, 64, Di] same dtype as q
@@ -150,11 +153,13 @@ class Indexer:
     k_scale: torch.Tensor = None
 
     def c(self) -> IndexerC:
-        mx = self.q_scale is not None and self.q_scale.dtype == torch.uint8
-        per_head = int(not mx and self.q_scale is not None and self.q_scale.dim() == 2)
-        code = SIA_MXFP8_E4M3 if mx else dtype_code(self.q)
+        coded_keys = self.k_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
+        mx = coded_keys and self.k_scale is not None and self.k_scale.dtype == torch.uint8
+        q_bf16 = int(coded_keys and self.q.dtype == torch.bfloat16)
+        per_head = int(not mx and not q_bf16 and self.q_scale is not None and self.q_scale.dim() == 2)
+        code = SIA_MXFP8_E4M3 if mx else (SIA_FP8_E4M3 if coded_keys else dtype_code(self.q))
         return IndexerC(_ptr(self.q), _ptr(self.q_scale), _ptr(self.w), _ptr(self.k_pool), _ptr(self.k_scale),
-                        code, per_head, self.q.shape[1], self.q.shape[2])
+                        code, per_head, self.q.shape[1], self.q.shape[2], q_bf16)
 
 
 @dataclass
@@ -228,6 +233,20 @@ def index_topk(ix: Indexer, seq: SeqMap, K: int, order: int = 0, method: int = 0
     _check(lib().sia_index_topk(ctypes.byref(a), ctypes.byref(s), K, order, method, _ptr(idx), _ptr(vals), _ptr(ws),
                                 nbytes, _stream(stream)))
     return (idx, vals) if with_vals else idx
+
+
+def quantize_indexer_q(ix: Indexer, stream=None):
+    """bf16 queries of `ix` -> (e4m3 codes [T, Hi, Di], scales): float [T] for
+    fp8 keys, uint8 E8M0 [T, Hi, Di/32] for MXFP8 keys."""
+    a = ix.c()
+    T, Hi, Di = ix.q.shape
+    codes = torch.empty(T, Hi, Di, dtype=torch.uint8, device=ix.q.device)
+    if a.dtype == SIA_MXFP8_E4M3:
+        scales = torch.empty(T, Hi, Di // 32, dtype=torch.uint8, device=ix.q.device)
+    else:
+        scales = torch.empty(T, dtype=torch.float32, device=ix.q.device)
+    _check(lib().sia_quantize_indexer_q(ctypes.byref(a), T, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
 
 
 def index_topk_method(ix: Indexer, seq: SeqMap) -> str:

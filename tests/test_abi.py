@@ -67,7 +67,7 @@ def good_seq(**kw):
 
 def good_indexer(**kw):
     d = dict(q=FAKE, q_scale=FAKE, w=FAKE, k_pool=FAKE, k_scale=FAKE, dtype=sia.SIA_FP8_E4M3,
-             q_scale_per_head=0, heads=64, dim=128)
+             q_scale_per_head=0, heads=64, dim=128, q_bf16=0)
     d.update(kw)
     return sia.IndexerC(**d)
 
@@ -102,6 +102,23 @@ def test_seqmap_validation(Lcpu, kw, code):
 def test_indexer_validation(Lcpu, kw, code):
     L = Lcpu
     assert call_scores(L, good_indexer(**kw), good_seq()) == code
+
+
+def test_bf16_query_validation(Lcpu):
+    L = Lcpu
+    # the score entry point takes quantized queries only
+    assert call_scores(L, good_indexer(q_bf16=1), good_seq()) == -2
+    assert call_scores(L, good_indexer(q_bf16=2), good_seq()) == -1
+    assert call_scores(L, good_indexer(q_bf16=1, dtype=sia.SIA_F32, heads=4, dim=32), good_seq()) == -2
+    qz = lambda ix, codes=FAKE, scales=FAKE, T=4: L.sia_quantize_indexer_q(
+        ctypes.byref(ix), T, ctypes.c_void_p(codes) if codes else None, ctypes.c_void_p(scales) if scales else None,
+        None)
+    assert qz(good_indexer(q_bf16=0)) == -1
+    assert qz(good_indexer(q_bf16=1), codes=0) == -1
+    assert qz(good_indexer(q_bf16=1), codes=FAKE + 8) == -1
+    assert qz(good_indexer(q_bf16=1), T=-1) == -1
+    assert qz(good_indexer(q_bf16=1, heads=48)) == -2
+    assert qz(good_indexer(q_bf16=1, dtype=sia.SIA_MXFP8_E4M3), scales=FAKE + 1) == -1
 
 
 def test_scores_buffer_validation(Lcpu):

@@ -412,3 +412,62 @@ def test_index_scores_never_write_past_max_visible(name):
     for t in range(wl.Tq):
         n = int(wl.q_pos[t]) + 1
         assert np.all(np.isfinite(got[t, :n])), f"row {t}"
+
+
+# ---------------------------------------------------------------------------
+# Dynamic Q quantization (bf16 queries -> fp8 per token / MXFP8 per 32)
+
+def _bf16_queries(seed, T, Hi, Di=128):
+    """N(0,1) draws at mixed magnitudes, a token of zeros, tiny and large values."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, Hi, Di)).astype(np.float32)
+    x *= (10.0 ** rng.integers(-4, 4, size=(T, 1, 1))).astype(np.float32)
+    x[1] = 0.0
+    x[2, :, :32] = 0.0                                   # all-zero MX groups
+    x[3] *= np.float32(1e-30)                            # subnormal-range values
+    x[4, 0, 0] = 3.0e38                                  # near the bf16 maximum
+    return W.to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("Hi", [32, 64])
+def test_quantize_q_matches_oracle(mx, Hi):
+    print(f"[quantize-q] mx={mx} Hi={Hi}", flush=True)
+    bits = _bf16_queries(30 + Hi + mx, 37, Hi)
+    kpool = torch.zeros(1, 64, 128, dtype=torch.uint8, device="cuda")
+    kscale = torch.zeros(1, 64, 4, dtype=torch.uint8, device="cuda") if mx else torch.ones(1, 64, device="cuda")
+    ix = sia.Indexer(dev(bits), torch.ones(37, Hi, device="cuda"), kpool, None, kscale)
+    codes, scales = sia.quantize_indexer_q(ix)
+    torch.cuda.synchronize()
+    e_codes, e_scales = O.quantize_q_mx(bits) if mx else O.quantize_q_fp8(bits)
+    assert np.array_equal(codes.cpu().numpy(), e_codes)
+    if mx:
+        assert np.array_equal(scales.cpu().numpy(), e_scales)
+    else:
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), e_scales.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["decode_tiny", "mx_decode_tiny", "prefill_tiny", "mx_prefill_tiny"])
+def test_bf16_queries_quantized_in_the_call(name):
+    """index_topk / index_select_attend given bf16 queries equal the same calls
+    given the oracle's quantization of them (ids bit for bit)."""
+    wl = workload(name)
+    print(f"[bf16-q] {name}", flush=True)
+    K, Hi = wl.cfg["K"], wl.cfg["Hi"]
+    mx = wl.cfg["idx_dtype"] == "mxfp8"
+    seq, ix, q, kv = upload(wl)
+    bits = _bf16_queries(40, wl.Tq, Hi)
+    codes, sc = O.quantize_q_mx(bits) if mx else O.quantize_q_fp8(bits)
+    ix_b = sia.Indexer(dev(bits), ix.w, ix.k_pool, None, ix.k_scale)
+    ix_q = sia.Indexer(dev(codes), ix.w, ix.k_pool, dev(sc), ix.k_scale)
+    for m in (sia.INDEX_TOPK_ONCHIP, sia.INDEX_TOPK_SCORES):
+        a_ids, a_vals = sia.index_topk(ix_b, seq, K, method=m, with_vals=True)
+        b_ids, b_vals = sia.index_topk(ix_q, seq, K, method=m, with_vals=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a_ids, b_ids) and torch.equal(a_vals, b_vals), f"method {m}"
+    ia = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    ib = torch.empty_like(ia)
+    oa = sia.index_select_attend(ix_b, q, kv, seq, K, wl.softmax_scale, idx_out=ia)
+    ob = sia.index_select_attend(ix_q, q, kv, seq, K, wl.softmax_scale, idx_out=ib)
+    torch.cuda.synchronize()
+    assert torch.equal(ia, ib) and torch.equal(oa.view(torch.int16), ob.view(torch.int16))
