@@ -180,6 +180,9 @@ def key_rows(k_pool, k_scale, slots, k_mx=None):
     elif k_pool.dtype == np.uint8:
         vals = decode_e4m3(flat)
         sc = np.asarray(k_scale, dtype=np.float64).reshape(-1)[slots]
+    elif k_pool.dtype == np.uint16:                 # bfloat16 bit patterns
+        vals = decode_bf16(flat)
+        sc = np.ones(len(slots), dtype=np.float64)
     else:
         vals = flat.astype(np.float64)
         sc = np.ones(len(slots), dtype=np.float64)
@@ -244,6 +247,9 @@ def _q_index_row(idx, t):
     if idx.get("q_mx") is not None:
         qv = mx_values(q, idx["q_mx"][t])
         qs = np.ones(q.shape[0])
+    elif q.dtype == np.uint16:                       # bfloat16 path: no scales
+        qv = decode_bf16(q)
+        qs = np.ones(q.shape[0])
     elif q.dtype == np.uint8:
         qv = decode_e4m3(q)
         qs = np.asarray(idx["q_scale"][t], dtype=np.float64)
@@ -257,7 +263,9 @@ def _q_index_row(idx, t):
 def index_scores(idx, seq, rows=None) -> dict:
     """Scores for query rows `rows` (default: all).  Returns {t: float32 [q_pos[t]+1]}.
 
-    idx: dict with q [Tq,Hi,Di] (uint8 codes or f32), q_scale ([Tq] or [Tq,Hi],
+    idx: dict with q [Tq,Hi,Di] (uint8 codes, uint16 bfloat16 bits or f32; the
+    bfloat16 indexer path of [P2, section 3.2] and [P5, section 3.1] has no
+    scales), q_scale ([Tq] or [Tq,Hi],
     fp8 only), w [Tq,Hi], k [P,page,Di], k_scale [P,page] (fp8 only); MXFP8
     instead gives q_mx [Tq,Hi,Di/32] and k_mx [P,page,Di/32] E8M0 bytes.
     seq: dict with q_seq, q_pos, block_table, page_size.

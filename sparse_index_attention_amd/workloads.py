@@ -70,6 +70,16 @@ CONFIGS = {
                                   kv_dtype="bf16"),
     "decode_h64_tiny": dict(cid=16, kind="decode", B=3, ctx=[33, 500, 1300], Hi=32, Di=128,
                             idx_dtype="fp8", K=192, H=64, Dc=512, Dr=64, kv_dtype="bf16"),
+    # bfloat16 indexer (the precision path), otherwise as decode / prefill
+    "bf16_decode": dict(cid=6, kind="decode", B=64, ctx=32768, Hi=64, Di=128, idx_dtype="bf16",
+                        K=2048, H=128, Dc=512, Dr=64, kv_dtype="bf16"),
+    "bf16_decode_tiny": dict(cid=20, kind="decode", B=5, ctx=[1, 65, 500, 2100, 9000], Hi=64, Di=128,
+                             idx_dtype="bf16", K=256, H=128, Dc=512, Dr=64, kv_dtype="bf16"),
+    "bf16_prefill_tiny": dict(cid=21, kind="prefill", T=390, Hi=32, Di=128, idx_dtype="bf16", K=64,
+                              H=64, Dc=512, Dr=64, kv_dtype="bf16"),
+    "bf16_chunked_prefill_tiny": dict(cid=22, kind="chunked", ctx=[300, 1000, 77, 2100, 5],
+                                      new=[37, 130, 77, 9, 2], Hi=64, Di=128, idx_dtype="bf16", K=128,
+                                      H=128, Dc=512, Dr=64, kv_dtype="bf16"),
     # MXFP8 indexer (32-element groups with E8M0 scales), otherwise as decode / prefill
     "mx_decode": dict(cid=5, kind="decode", B=64, ctx=32768, Hi=64, Di=128, idx_dtype="mxfp8",
                       K=2048, H=128, Dc=512, Dr=64, kv_dtype="bf16"),
@@ -126,6 +136,8 @@ class Workload:
     def oracle_indexer(self):
         if self.cfg["idx_dtype"] == "mxfp8":
             return dict(q=self.iq, q_mx=self.iq_scale, w=self.iw, k=self.ik, k_mx=self.ik_scale)
+        if self.cfg["idx_dtype"] == "bf16":
+            return dict(q=self.iq, w=self.iw, k=self.ik)
         return dict(q=self.iq, q_scale=self.iq_scale, w=self.iw, k=self.ik, k_scale=self.ik_scale)
 
     def oracle_kv(self):
@@ -296,6 +308,11 @@ def make_workload(name: str, mla=True, indexer=True) -> Workload:
             wl.ik = _draw_rows(cid, 1, P * PAGE, (Di,), "normal", convert=kconv,
                                out_dtype=np.uint8).reshape(P, PAGE, Di)
             wl.iq_scale, wl.ik_scale = qsc, ksc.reshape(P, PAGE, Di // 32)
+        elif cfg["idx_dtype"] == "bf16":
+            wl.iq = _draw_rows(cid, 0, Tq, (Hi, Di), "normal", convert=lambda x, r0: to_bf16_bits(x),
+                               out_dtype=np.uint16)
+            wl.ik = _draw_rows(cid, 1, P * PAGE, (Di,), "normal", convert=lambda x, r0: to_bf16_bits(x),
+                               out_dtype=np.uint16).reshape(P, PAGE, Di)
         elif cfg["idx_dtype"] == "f32":
             wl.iq = _draw_rows(cid, 0, Tq, (Hi, Di), "normal")
             wl.ik = _draw_rows(cid, 1, P * PAGE, (Di,), "normal").reshape(P, PAGE, Di)

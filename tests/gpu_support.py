@@ -17,7 +17,7 @@ from sparse_index_attention_amd import workloads as W
 # for the fp8 MFMA path (its internal accumulation rounds at ~2^-14 of A) and
 # 2^-16 for the fp32 path.
 SCORE_REL = 1e-3
-SCORE_EPS = {"fp8": 2.0 ** -11, "mxfp8": 2.0 ** -11, "f32": 2.0 ** -16}
+SCORE_EPS = {"fp8": 2.0 ** -11, "mxfp8": 2.0 ** -11, "bf16": 2.0 ** -16, "f32": 2.0 ** -16}
 # Attention tolerance: |g - o| <= ATOL + RTOL |o| elementwise.
 ATT_TOL = {"bf16": (2e-2, 1e-2), "fp8": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
 LSE_ATOL = {"bf16": 2e-2, "fp8": 2e-2, "f32": 1e-4}
@@ -37,7 +37,7 @@ def workload(name):
 def upload(wl: W.Workload, device="cuda"):
     c = wl.cfg
     seq = sia.SeqMap(dev(wl.q_seq), dev(wl.q_pos), dev(wl.block_table), wl.num_pages, wl.max_visible)
-    if c["idx_dtype"] == "f32":
+    if c["idx_dtype"] in ("f32", "bf16"):
         ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik))
     else:
         ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik), dev(wl.iq_scale), dev(wl.ik_scale))
@@ -58,6 +58,8 @@ def score_bound_row(wl: W.Workload, t: int) -> np.ndarray:
     q = idx["q"][t]
     if idx.get("q_mx") is not None:
         qv, qs = O.mx_values(q, idx["q_mx"][t]), np.ones(q.shape[0])
+    elif q.dtype == np.uint16:
+        qv, qs = O.decode_bf16(q), np.ones(q.shape[0])
     elif q.dtype == np.uint8:
         qv = O.decode_e4m3(q)
         qs = np.full(q.shape[0], float(idx["q_scale"][t]))

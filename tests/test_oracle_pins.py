@@ -232,6 +232,20 @@ def test_mx_generator_roundtrip():
     assert np.all(amax <= 448 * s) and np.all(amax > 224 * s)   # the smallest power of two that fits
 
 
+def test_bf16_indexer_rows_brute_force():
+    """bfloat16 queries and keys: the score of the exact decoded values, no scales."""
+    wl = W.make_workload("bf16_decode_tiny", mla=False)
+    t = 2
+    sc = O.index_scores(wl.oracle_indexer(), wl.oracle_seq(), [t])[t]
+    qv = O.decode_bf16(wl.iq[t])
+    assert np.array_equal(qv.astype(np.float32), qv)                     # bf16 values are exact in f32
+    for s in [0, 1, 63, 64, int(wl.q_pos[t])]:
+        slot = wl.block_table[t][s // 64] * 64 + s % 64
+        kk = O.decode_bf16(wl.ik.reshape(-1, 128)[slot])
+        ref = _brute_scores(qv, np.ones(64), wl.iw[t], kk[None], np.ones(1))[0]
+        assert sc[s] == np.float32(ref)
+
+
 def test_encode_e4m3_grid_ties_and_saturation():
     codes = np.arange(256, dtype=np.uint8)
     finite = codes[(codes & 0x7F) != 0x7F]
