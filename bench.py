@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill", "mx_decode"])
+                   choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill", "mx_decode", "bf16_decode"])
     p.add_argument("--copies", type=int, default=3, help="distinct device copies of the inputs (decode)")
     p.add_argument("--order", type=int, default=0, help="Top-K output order (0 score-sorted, 1 by position)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle baseline")
@@ -138,6 +138,8 @@ def algorithmic_work(wl):
     sel = vis.clip(max=K)
     if c["idx_dtype"] == "mxfp8":          # codes + one E8M0 byte per 32 elements
         key_b, q_b = Di + Di // 32, Hi * (Di + Di // 32) + 4 * Hi
+    elif c["idx_dtype"] == "bf16":
+        key_b, q_b = 2 * Di, Hi * 2 * Di + 4 * Hi
     else:
         key_b = Di + 4 if c["idx_dtype"] == "fp8" else 4 * Di
         q_b = Hi * Di * (1 if c["idx_dtype"] == "fp8" else 4) + 4 * Hi + 4
@@ -230,7 +232,7 @@ def main():
     for i in range(copies):
         if base is None:
             seq = sia.SeqMap(dev(wl.q_seq), dev(wl.q_pos), dev(wl.block_table), wl.num_pages, wl.max_visible)
-            if c["idx_dtype"] == "f32":
+            if c["idx_dtype"] in ("f32", "bf16"):
                 ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik))
             else:
                 ix = sia.Indexer(dev(wl.iq), dev(wl.iw), dev(wl.ik), dev(wl.iq_scale), dev(wl.ik_scale))
@@ -375,7 +377,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2), "wall_s": round(wall, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"fp8": "fp8+bf16", "mxfp8": "mxfp8+bf16"}.get(c["idx_dtype"], "f32"), "data": "synthetic",
+        "dtype": {"fp8": "fp8+bf16", "mxfp8": "mxfp8+bf16", "bf16": "bf16"}.get(c["idx_dtype"], "f32"), "data": "synthetic",
         "config": cfg, "breakdown_us": breakdown, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

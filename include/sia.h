@@ -83,8 +83,9 @@ typedef struct {
 } sia_seqmap;
 
 /* Indexer inputs [P1, "Sparse Attention Pipeline Optimization"; P2, section 3.1].
- *   q        [T, heads, dim]  e4m3 codes (SIA_FP8_E4M3, SIA_MXFP8_E4M3) or
- *            float (SIA_F32); with q_bf16 = 1, bfloat16 queries that are
+ *   q        [T, heads, dim]  e4m3 codes (SIA_FP8_E4M3, SIA_MXFP8_E4M3),
+ *            bfloat16 (SIA_BF16: the precision path, no scales [P2, section
+ *            3.2; P5, section 3.1]) or float (SIA_F32); with q_bf16 = 1, bfloat16 queries that are
  *            quantized on the fly to the indexer's format (see
  *            sia_quantize_indexer_q); q_scale is then unused
  *   q_scale  SIA_FP8_E4M3: float [T] (q_scale_per_head = 0) or [T, heads] (= 1)
@@ -97,7 +98,7 @@ typedef struct {
  *   k_scale  SIA_FP8_E4M3: float [num_pages, page_size], one per key token
  *            SIA_MXFP8_E4M3: uint8 [num_pages, page_size, dim/32] E8M0 group
  *            scales; 4-byte aligned
- * Supported: SIA_F32 with heads <= 64, dim <= 256; SIA_FP8_E4M3 and
+ * Supported: SIA_F32 with heads <= 64, dim <= 256; SIA_BF16, SIA_FP8_E4M3 and
  * SIA_MXFP8_E4M3 with heads in {32, 64} and dim = 128.                        */
 typedef struct {
   const void* q;

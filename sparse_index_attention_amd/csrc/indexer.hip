@@ -306,6 +306,7 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
   const IndexArgs a = index_args(in, s, scores, ld);
   if (s.T == 0 || s.max_visible == 0) return hipSuccess;
   const bool mx = in.dtype == SIA_MXFP8_E4M3;
+  if (in.dtype == SIA_BF16) return launch_index_scores_bf16(in, s, scores, ld, st);
   if (in.dtype == SIA_F32) {
     dim3 grid(s.T, (s.max_visible + 255) / 256);
     hipLaunchKernelGGL(k_index_scores_f32, grid, dim3(256), 0, st, a);

@@ -43,7 +43,11 @@ static int check_indexer(const sia_indexer_in* in) {
   if (!in || !in->q || !in->w || !in->k_pool) return SIA_ERR_INVALID_ARG;
   if (in->heads < 1 || in->dim < 1) return SIA_ERR_INVALID_ARG;
   if (in->q_bf16 != 0 && in->q_bf16 != 1) return SIA_ERR_INVALID_ARG;
-  if (in->dtype == SIA_F32) {
+  if (in->dtype == SIA_BF16) {
+    if (in->q_bf16) return SIA_ERR_UNSUPPORTED;   // q already bfloat16
+    if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
+    if (!aligned16(in->q) || !aligned16(in->k_pool)) return SIA_ERR_INVALID_ARG;
+  } else if (in->dtype == SIA_F32) {
     if (in->q_bf16) return SIA_ERR_UNSUPPORTED;
     if (in->heads > 64 || (int64_t)in->heads * in->dim > 4096) return SIA_ERR_UNSUPPORTED;
   } else if (in->dtype == SIA_FP8_E4M3 || in->dtype == SIA_MXFP8_E4M3) {

@@ -41,6 +41,9 @@ hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K,
                        float* vals, hipStream_t st);
 hipError_t launch_topk_candidates(const float* cscore, const int32_t* cpos, int64_t ldc, int range_keys,
                                   const SeqArgs& s, int K, int order, int32_t* idx, float* vals, hipStream_t st);
+// indexer_bf16.hip
+hipError_t launch_index_scores_bf16(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,
+                                    hipStream_t st);
 // quantize.hip
 hipError_t launch_quantize_q(const void* q_bf16, int T, int heads, int dim, bool mx, uint8_t* codes, void* scales,
                              hipStream_t st);

@@ -21,7 +21,7 @@ from gpu_support import check_attention, check_scores, dev, kind_of, tie_band_ok
 pytestmark = pytest.mark.gpu
 
 # name -> number of sampled query rows
-CASES = {"decode": 6, "quant_decode": 3, "long_prefill": 10, "cp_chunk_prefill": 8, "mx_decode": 3}
+CASES = {"decode": 6, "quant_decode": 3, "long_prefill": 10, "cp_chunk_prefill": 8, "mx_decode": 3, "bf16_decode": 3}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -72,7 +72,7 @@ def test_full_size(name):
     torch.cuda.empty_cache()
 
     # steps 1 + 2: the on-chip method and the score-matrix method agree exactly
-    if wl.cfg["kind"] == "decode":
+    if wl.cfg["kind"] == "decode" and wl.cfg["idx_dtype"] in ("fp8", "mxfp8"):
         a_ids, a_vals = sia.index_topk(ix, seq, K, method=sia.INDEX_TOPK_ONCHIP, with_vals=True)
         b_ids, b_vals = sia.index_topk(ix, seq, K, method=sia.INDEX_TOPK_SCORES, with_vals=True)
         torch.cuda.synchronize()

@@ -17,7 +17,8 @@ from gpu_support import (check_attention, check_scores, dev, kind_of, tie_band_o
 pytestmark = pytest.mark.gpu
 
 TINY = ["tiny_prefill", "decode_tiny", "prefill_tiny", "quant_decode_tiny", "quant_decode_tile128_tiny",
-        "cp_chunk_prefill_tiny", "decode_h64_tiny", "chunked_prefill_tiny", "mx_decode_tiny", "mx_prefill_tiny"]
+        "cp_chunk_prefill_tiny", "decode_h64_tiny", "chunked_prefill_tiny", "mx_decode_tiny", "mx_prefill_tiny",
+        "bf16_decode_tiny", "bf16_prefill_tiny", "bf16_chunked_prefill_tiny"]
 
 
 @pytest.fixture(scope="module", autouse=True)
