@@ -38,7 +38,7 @@ import numpy as np
 __all__ = [
     "decode_e4m3", "decode_bf16", "decode_e8m0", "mx_values", "encode_e4m3", "quantize_q_fp8", "quantize_q_mx",
     "physical_slots", "key_rows", "kv_rows",
-    "index_scores_row", "index_scores", "topk_row", "topk", "sparse_mla_row",
+    "index_scores_row", "index_scores", "topk_row", "topk", "topk_pages_row", "topk_pages", "sparse_mla_row",
     "sparse_mla", "merge_partials", "index_select_attend",
 ]
 
@@ -317,6 +317,42 @@ def topk(scores: dict, K, order=0) -> dict:
     return {t: topk_row(s, K, order) for t, s in scores.items()}
 
 
+def topk_pages_row(scores_f32, K, page=64):
+    """Block-aligned selection of one row of float32 scores, int32 [K].
+
+    [P3, section 3.1] aligns the selection to cache blocks so that attention
+    reads the cache in whole blocks.  The page does not say how a block is
+    ranked; the reading taken here: a block of `page` consecutive positions
+    scores the largest score among its visible positions (a block is kept when
+    it holds one of the strongest positions), the first min(K / page, blocks)
+    blocks under (block score descending, block index ascending) are kept, and
+    every visible position of a kept block is emitted, blocks in ascending
+    order, -1 padding up to K.  K must be a multiple of `page`.  With page = 1
+    this is topk_row(order=1).  Scores must be finite.
+    """
+    assert K % page == 0, "block-aligned selection takes whole blocks"
+    s = np.asarray(scores_f32, dtype=np.float32).astype(np.float64)
+    assert np.all(np.isfinite(s)), "Top-K contract covers finite scores only"
+    s = s + 0.0                                    # -0.0 + 0.0 == +0.0
+    n = s.shape[0]
+    n_blocks = -(-n // page)
+    best = np.array([s[b * page: min(n, (b + 1) * page)].max() for b in range(n_blocks)])
+    perm = np.lexsort((np.arange(n_blocks), -best))
+    kept = np.sort(perm[: min(K // page, n_blocks)])
+    out = np.full(K, -1, dtype=np.int32)
+    at = 0
+    for b in kept:
+        cols = np.arange(b * page, min(n, (b + 1) * page))
+        out[at: at + cols.shape[0]] = cols
+        at += cols.shape[0]
+    return out
+
+
+def topk_pages(scores: dict, K, page=64) -> dict:
+    """Block-aligned selection for every row of a {t: float32 scores} dict."""
+    return {t: topk_pages_row(s, K, page) for t, s in scores.items()}
+
+
 # ---------------------------------------------------------------------------
 # Step 3: sparse MLA attention over the selected rows
 # ---------------------------------------------------------------------------
@@ -390,12 +426,14 @@ def merge_partials(outs, lses):
 def index_select_attend(idx, q, kv, seq, K, scale, rows=None, order=0):
     """Scores -> Top-K -> sparse MLA for the given query rows.
 
+    order 0 / 1: per-position Top-K in score / position order; order 2: the
+    block-aligned selection of topk_pages_row with the cache's page size.
     Returns (scores {t: f32}, selected {t: int32 [K]}, attention {t: (out, lse)}).
     [P1, "Sparse Attention Pipeline Optimization"] pseudo-code: the indexer
     scores and weights, Top-K picks positions, the sparse kernel gathers and
     attends.
     """
     sc = index_scores(idx, seq, rows)
-    sel = topk(sc, K, order)
+    sel = topk_pages(sc, K, seq["page_size"]) if order == 2 else topk(sc, K, order)
     att = sparse_mla(q, kv, seq, sel, scale)
     return sc, sel, att

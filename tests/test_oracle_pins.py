@@ -336,6 +336,88 @@ def test_topk_invariants():
 
 
 # ---------------------------------------------------------------------------
+# block-aligned selection ([P3, section 3.1]; block score = the largest score
+# among the block's visible positions, a reading)
+# ---------------------------------------------------------------------------
+def _brute_pages(s, K, page):
+    """Block selection by rank counting with plain loops: block b is kept when
+    fewer than K/page blocks beat it (higher best score, or equal and lower)."""
+    n = len(s)
+    nb = (n + page - 1) // page
+    best = []
+    for b in range(nb):
+        m = None
+        for i in range(b * page, min(n, b * page + page)):
+            v = float(s[i]) + 0.0
+            m = v if m is None or v > m else m
+        best.append(m)
+    out = []
+    for b in range(nb):
+        beaten_by = sum(1 for c in range(nb) if best[c] > best[b] or (best[c] == best[b] and c < b))
+        if beaten_by < K // page:
+            out.extend(range(b * page, min(n, b * page + page)))
+    return np.array(out + [-1] * (K - len(out)), dtype=np.int32)
+
+
+@pytest.mark.parametrize("n,K,page", [(1, 4, 4), (10, 8, 4), (37, 12, 4), (64, 16, 8), (130, 64, 64),
+                                      (200, 64, 16), (1000, 128, 64)])
+def test_topk_pages_vs_rank_counting(n, K, page):
+    rng = np.random.default_rng(n * 7 + K + page)
+    s = np.round(rng.standard_normal(n) * 3).astype(np.float32)     # many ties
+    assert np.array_equal(O.topk_pages_row(s, K, page), _brute_pages(s, K, page))
+
+
+def test_topk_pages_worked_case_max_not_sum():
+    # four blocks of 4: maxima 9, 5, 8, 1 and sums 9, 20, 8, 4.  Two blocks are
+    # kept: by the maximum blocks 0 and 2; a sum rule would keep 1 and 0, and the
+    # per-position Top-8 would mix all four blocks.
+    s = np.array([0, 0, 0, 9, 5, 5, 5, 5, 8, 0, 0, 0, 1, 1, 1, 1], dtype=np.float32)
+    assert list(O.topk_pages_row(s, 8, 4)) == [0, 1, 2, 3, 8, 9, 10, 11]
+    assert sorted(O.topk_row(s, 8)) != [0, 1, 2, 3, 8, 9, 10, 11]
+
+
+def test_topk_pages_partial_last_block_and_ties():
+    # 10 visible positions in blocks of 4: the last block holds positions 8, 9
+    s = np.array([1, 1, 1, 1, 0, 0, 0, 0, 3, 2], dtype=np.float32)
+    assert list(O.topk_pages_row(s, 8, 4)) == [0, 1, 2, 3, 8, 9, -1, -1]
+    # equal block maxima (including -0.0 against +0.0) go to the lower block
+    t = np.array([0, -0.0, 0, 0, 0, 0, 0, 0, -0.0, -0.0, 0, 0], dtype=np.float32)
+    assert list(O.topk_pages_row(t, 4, 4)) == [0, 1, 2, 3]
+    assert list(O.topk_pages_row(t, 8, 4)) == [0, 1, 2, 3, 4, 5, 6, 7]
+
+
+def test_topk_pages_block_of_one_is_position_topk():
+    rng = np.random.default_rng(11)
+    for n, K in ((1, 1), (9, 4), (300, 32), (50, 64)):
+        s = np.round(rng.standard_normal(n) * 2).astype(np.float32)
+        assert np.array_equal(O.topk_pages_row(s, K, 1), O.topk_row(s, K, order=1))
+
+
+def test_topk_pages_invariants():
+    rng = np.random.default_rng(12)
+    page = 64
+    for n in (1, 63, 64, 65, 2047, 2048, 2049, 5000):
+        s = rng.standard_normal(n).astype(np.float32)
+        for K in (64, 256, 2048):
+            idx = O.topk_pages_row(s, K, page)
+            sel = idx[idx >= 0]
+            assert np.all(idx[len(sel):] == -1)                      # padding trails
+            assert np.all(np.diff(sel) > 0) and np.all(sel < n)      # ascending, visible
+            blocks = np.unique(sel // page)
+            assert len(blocks) == min(K // page, -(-n // page))
+            for b in blocks:                                         # whole blocks
+                assert np.array_equal(sel[sel // page == b], np.arange(b * page, min(n, b * page + page)))
+            if n <= K:
+                assert np.array_equal(sel, np.arange(n))
+            best = np.array([s[b * page: b * page + page].max() for b in range(-(-n // page))])
+            kept_min = best[blocks].min()
+            others = np.setdiff1d(np.arange(len(best)), blocks)
+            assert not np.any(best[others] > kept_min)
+            # the block holding the best position is always kept
+            assert int(np.argmax(s)) in set(sel.tolist())
+
+
+# ---------------------------------------------------------------------------
 # sparse MLA
 # ---------------------------------------------------------------------------
 def test_mla_dense_equals_sdpa_when_K_covers_context():
