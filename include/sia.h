@@ -137,7 +137,15 @@ typedef struct {
 
 /* Operation codes for sia_workspace_size. */
 enum { SIA_OP_TOPK = 0, SIA_OP_MLA_DECODE = 1, SIA_OP_MLA_PREFILL = 2, SIA_OP_INDEX_SELECT_ATTEND = 3,
-       SIA_OP_INDEX_TOPK = 4 };
+       SIA_OP_INDEX_TOPK = 4, SIA_OP_TOPK_PAGES = 5 };
+
+/* Values of the `order` argument of the selecting calls.
+ *   SIA_ORDER_SCORE     per-position Top-K, written best first
+ *   SIA_ORDER_POSITION  the same set, written in ascending position
+ *   SIA_SELECT_PAGES    block-aligned selection (sia_topk_pages): whole pages
+ *                       of the cache, positions written in ascending order;
+ *                       K must be a multiple of the page size (64)           */
+enum { SIA_ORDER_SCORE = 0, SIA_ORDER_POSITION = 1, SIA_SELECT_PAGES = 2 };
 
 /* Step 1 — indexer scores [P1, "Sparse Attention Pipeline Optimization";
  * P2, section 3.1; P3, section 3.1].
@@ -162,6 +170,24 @@ int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* sco
 int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, int32_t order,
              int32_t* idx, float* vals, hipStream_t stream);
 
+/* Step 2, block-aligned form [P3, section 3.1: the selection is aligned to
+ * cache blocks so that attention reads the cache block by block].  The page
+ * leaves the block ranking open; here a page (64 consecutive positions, the
+ * cache block) scores the largest of scores[t * ld + s] over its positions
+ * s <= q_pos[t].  Keeps the first min(K / 64, pages) pages under (page score
+ * descending, page ascending), -0.0 equal to +0.0, and writes every visible
+ * position of the kept pages in ascending order, then -1 up to K (so the -1
+ * entries trail).  Rows with q_pos[t] + 1 <= K keep every visible position.
+ * Scores must be finite.
+ *   idx   [T, K] int32 logical positions
+ *   vals  [T, K] float or NULL: each position's page score (-inf for padding)
+ *   ws    at least sia_workspace_size(SIA_OP_TOPK_PAGES, ...) bytes, 256-byte
+ *         aligned (page scores and the kept pages)
+ * Supported: K a multiple of 64, 64 <= K <= 2048 (else SIA_ERR_INVALID_ARG /
+ * SIA_ERR_UNSUPPORTED).                                                        */
+int sia_topk_pages(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, int32_t* idx,
+                   float* vals, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Steps 1 + 2 fused — indexer scores and per-query Top-K without a score
  * matrix in memory [P1, "Sparse Attention Pipeline Optimization" (indexer
  * fusion); P4, section 2; P5, section 3.1].  Same result as sia_index_scores
@@ -177,6 +203,8 @@ int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, 
  *   SIA_INDEX_TOPK_AUTO    the on-chip method for fp8 and MXFP8 indexers when there are
  *       at most two queries per sequence on average and at least one
  *       (query, range) pair per compute unit; the score matrix otherwise.
+ * order = SIA_SELECT_PAGES gives sia_topk_pages' block-aligned selection (the
+ * score-matrix method; SIA_INDEX_TOPK_ONCHIP is then SIA_ERR_UNSUPPORTED).
  *   ws  workspace of at least sia_workspace_size(SIA_OP_INDEX_TOPK, ...) bytes
  *       (enough for either method), 256-byte aligned; heads and latent_dim
  *       are ignored for this op.
@@ -236,7 +264,8 @@ int sia_sparse_mla_prefill(const void* q, sia_dtype q_dtype, int32_t heads, cons
  * run as sia_index_topk with SIA_INDEX_TOPK_AUTO; its scratch and (when
  * idx_out is NULL) the indices live in the workspace.  Uses the split
  * (decode) attention when there are too few tokens to fill the GPU.
- *   idx_out [T, K] int32 or NULL; `order` as in sia_topk.                     */
+ *   idx_out [T, K] int32 or NULL; `order` as in sia_topk, or SIA_SELECT_PAGES
+ *           for the block-aligned selection of sia_topk_pages.                */
 int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dtype q_dtype,
                             int32_t heads, const sia_kv_in* kv, const sia_seqmap* seq, int32_t K,
                             int32_t order, float softmax_scale, int32_t* idx_out, void* out,

@@ -132,11 +132,23 @@ constexpr size_t kQCodesPerToken = 64 * 128, kQScalesPerToken = 64 * 4;
 static size_t q_ws_bytes(const sia_seqmap& seq) {
   return align256((size_t)seq.num_tokens * kQCodesPerToken) + align256((size_t)seq.num_tokens * kQScalesPerToken);
 }
+// The score-matrix method keeps room for the block-aligned selection behind the matrix.
+static size_t matrix_bytes(const sia_seqmap& seq) {
+  return align256((size_t)seq.num_tokens * fused_ld(&seq) * sizeof(float));
+}
 static size_t index_topk_ws_bytes(const sia_seqmap& seq, int K) {
   const size_t cand = (size_t)seq.num_tokens * index_topk_ld(seq.max_visible, K);
   const size_t onchip = 2 * align256(cand * sizeof(float));
-  const size_t matrix = align256((size_t)seq.num_tokens * fused_ld(&seq) * sizeof(float));
+  const size_t matrix = matrix_bytes(seq) + topk_pages_ws_bytes(seq.num_tokens, seq.max_visible, K);
   return q_ws_bytes(seq) + (onchip > matrix ? onchip : matrix);
+}
+
+// Checks of K and `order` shared by the selecting entry points.
+static int check_select(int K, int order) {
+  if (K < 1 || order < SIA_ORDER_SCORE || order > SIA_SELECT_PAGES) return SIA_ERR_INVALID_ARG;
+  if (order == SIA_SELECT_PAGES && K % 64 != 0) return SIA_ERR_INVALID_ARG;
+  if (K > 2048) return SIA_ERR_UNSUPPORTED;
+  return SIA_OK;
 }
 
 // With bf16 queries: quantize them into the workspace and describe the result
@@ -170,8 +182,10 @@ static hipError_t run_index_topk(int method, const sia_indexer_in& in_given, con
   float* scores = static_cast<float*>(ws);
   const int64_t ld = fused_ld(&seq);
   hipError_t e = launch_index_scores(in, s, scores, ld, stream);
-  if (e == hipSuccess) e = launch_topk(scores, ld, s, K, order, idx, vals, stream);
-  return e;
+  if (e != hipSuccess) return e;
+  if (order == SIA_SELECT_PAGES)
+    return launch_topk_pages(scores, ld, s, K, idx, vals, static_cast<unsigned char*>(ws) + matrix_bytes(seq), stream);
+  return launch_topk(scores, ld, s, K, order, idx, vals, stream);
 }
 
 extern "C" {
@@ -210,6 +224,22 @@ int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, 
   if (rc) return rc;
   if (K < 1 || K > 2048 || (order != 0 && order != 1) || !idx) return K > 2048 ? SIA_ERR_UNSUPPORTED : SIA_ERR_INVALID_ARG;
   const hipError_t e = launch_topk(scores, ld, seq_args(*seq), K, order, idx, vals, stream);
+  return e == hipSuccess ? SIA_OK : hip_fail(e);
+}
+
+int sia_topk_pages(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, int32_t* idx, float* vals,
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_seq(seq);
+  if (rc) return rc;
+  rc = check_scores(scores, ld, seq);
+  if (rc) return rc;
+  if (!idx) return SIA_ERR_INVALID_ARG;
+  rc = check_select(K, SIA_SELECT_PAGES);
+  if (rc) return rc;
+  if (seq->num_tokens == 0) return SIA_OK;
+  const size_t need = sia_workspace_size(SIA_OP_TOPK_PAGES, seq, K, 1, 1);
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
+  const hipError_t e = launch_topk_pages(scores, ld, seq_args(*seq), K, idx, vals, ws, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);
 }
 
@@ -253,6 +283,8 @@ size_t sia_workspace_size(int32_t op, const sia_seqmap* seq, int32_t K, int32_t 
       return mla_workspace_bytes(T, K, heads, latent_dim);
     case SIA_OP_INDEX_TOPK:
       return T == 0 ? 0 : index_topk_ws_bytes(*seq, K);
+    case SIA_OP_TOPK_PAGES:
+      return T == 0 ? 0 : topk_pages_ws_bytes(T, seq->max_visible, K);
     case SIA_OP_INDEX_SELECT_ATTEND: {
       if (T == 0) return 0;
       const size_t scores = index_topk_ws_bytes(*seq, K);
@@ -270,15 +302,18 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
   if (rc) return rc;
   rc = check_indexer(in);
   if (rc) return rc;
-  if (K < 1 || (order != 0 && order != 1) || !idx) return SIA_ERR_INVALID_ARG;
+  if (!idx) return SIA_ERR_INVALID_ARG;
   if (method < SIA_INDEX_TOPK_AUTO || method > SIA_INDEX_TOPK_SCORES) return SIA_ERR_INVALID_ARG;
-  if (K > 2048) return SIA_ERR_UNSUPPORTED;
-  if (method == SIA_INDEX_TOPK_ONCHIP && in->dtype != SIA_FP8_E4M3 && in->dtype != SIA_MXFP8_E4M3)
+  rc = check_select(K, order);
+  if (rc) return rc;
+  if (method == SIA_INDEX_TOPK_ONCHIP &&
+      ((in->dtype != SIA_FP8_E4M3 && in->dtype != SIA_MXFP8_E4M3) || order == SIA_SELECT_PAGES))
     return SIA_ERR_UNSUPPORTED;
   if (seq->num_tokens == 0) return SIA_OK;
   const size_t need = sia_workspace_size(SIA_OP_INDEX_TOPK, seq, K, 1, 1);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
-  if (method == SIA_INDEX_TOPK_AUTO) method = index_topk_auto(*in, *seq);
+  if (method == SIA_INDEX_TOPK_AUTO)
+    method = order == SIA_SELECT_PAGES ? SIA_INDEX_TOPK_SCORES : index_topk_auto(*in, *seq);
   const hipError_t e = run_index_topk(method, *in, *seq, K, order, idx, vals, ws, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);
 }
@@ -311,8 +346,8 @@ int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dty
   if (rc) return rc;
   rc = check_indexer(in);
   if (rc) return rc;
-  if (K < 1 || (order != 0 && order != 1)) return SIA_ERR_INVALID_ARG;
-  if (K > 2048) return SIA_ERR_UNSUPPORTED;
+  rc = check_select(K, order);
+  if (rc) return rc;
   rc = mla_common(q_mla, q_dtype, heads, kv, seq, idx_out ? idx_out : (const int32_t*)ws, K, softmax_scale, out);
   if (rc) return rc;
   if (seq->num_tokens == 0) return SIA_OK;
@@ -327,7 +362,8 @@ int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dty
   void* mla_ws = base;
 
   const SeqArgs s = seq_args(*seq);
-  hipError_t e = run_index_topk(index_topk_auto(*in, *seq), *in, *seq, K, order, ids, nullptr, sel_ws, stream);
+  const int method = order == SIA_SELECT_PAGES ? SIA_INDEX_TOPK_SCORES : index_topk_auto(*in, *seq);
+  hipError_t e = run_index_topk(method, *in, *seq, K, order, ids, nullptr, sel_ws, stream);
   if (e != hipSuccess) return hip_fail(e);
   const int splits = kv->dtype == SIA_F32 ? 1 : mla_splits(T, K, heads);
   e = launch_sparse_mla(q_mla, heads, *kv, s, ids, K, softmax_scale, out, lse, splits, mla_ws, stream);

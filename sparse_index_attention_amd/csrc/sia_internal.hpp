@@ -41,6 +41,11 @@ hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K,
                        float* vals, hipStream_t st);
 hipError_t launch_topk_candidates(const float* cscore, const int32_t* cpos, int64_t ldc, int range_keys,
                                   const SeqArgs& s, int K, int order, int32_t* idx, float* vals, hipStream_t st);
+// topk_pages.hip: block-aligned selection (whole 64-position pages, ascending)
+int64_t topk_pages_ld(int max_visible);
+size_t topk_pages_ws_bytes(int T, int max_visible, int K);
+hipError_t launch_topk_pages(const float* scores, int64_t ld, const SeqArgs& s, int K, int32_t* idx, float* vals,
+                             void* ws, hipStream_t st);
 // indexer_bf16.hip
 hipError_t launch_index_scores_bf16(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,
                                     hipStream_t st);

@@ -17,7 +17,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsia.so"
 _lib = None
 
 SIA_F32, SIA_BF16, SIA_FP8_E4M3, SIA_MXFP8_E4M3 = 0, 1, 2, 3
-OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_INDEX_SELECT_ATTEND, OP_INDEX_TOPK = 0, 1, 2, 3, 4
+OP_TOPK, OP_MLA_DECODE, OP_MLA_PREFILL, OP_INDEX_SELECT_ATTEND, OP_INDEX_TOPK, OP_TOPK_PAGES = 0, 1, 2, 3, 4, 5
+ORDER_SCORE, ORDER_POSITION, SELECT_PAGES = 0, 1, 2
 INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP, INDEX_TOPK_SCORES = 0, 1, 2
 
 c_i32, c_i64, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -58,6 +59,7 @@ def lib():
         P = ctypes.POINTER
         L.sia_index_scores.argtypes = [P(IndexerC), P(SeqMapC), c_p, c_i64, c_p]
         L.sia_topk.argtypes = [c_p, c_i64, P(SeqMapC), c_i32, c_i32, c_p, c_p, c_p]
+        L.sia_topk_pages.argtypes = [c_p, c_i64, P(SeqMapC), c_i32, c_p, c_p, c_p, ctypes.c_size_t, c_p]
         L.sia_index_topk_method.argtypes = [P(IndexerC), P(SeqMapC)]
         L.sia_quantize_indexer_q.argtypes = [P(IndexerC), c_i32, c_p, c_p, c_p]
         L.sia_index_topk.argtypes = [P(IndexerC), P(SeqMapC), c_i32, c_i32, c_i32, c_p, c_p, c_p, ctypes.c_size_t,
@@ -217,10 +219,27 @@ def topk(scores: torch.Tensor, seq: SeqMap, K: int, order: int = 0, idx=None, va
     return (idx, vals) if with_vals else idx
 
 
+def topk_pages(scores: torch.Tensor, seq: SeqMap, K: int, idx=None, vals=None, with_vals=False, ws=None,
+               stream=None):
+    """Block-aligned selection (sia_topk_pages): whole 64-position pages ranked by
+    their best visible score, positions in ascending order, -1 padding."""
+    T = seq.num_tokens
+    if idx is None:
+        idx = torch.empty(T, K, dtype=torch.int32, device=scores.device)
+    if with_vals and vals is None:
+        vals = torch.empty(T, K, dtype=torch.float32, device=scores.device)
+    ws = _workspace(ws, workspace_size(OP_TOPK_PAGES, seq, K, 1, 1), scores.device)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    s = seq.c()
+    _check(lib().sia_topk_pages(_ptr(scores), scores.shape[1], ctypes.byref(s), K, _ptr(idx), _ptr(vals), _ptr(ws),
+                                nbytes, _stream(stream)))
+    return (idx, vals) if with_vals else idx
+
+
 def index_topk(ix: Indexer, seq: SeqMap, K: int, order: int = 0, method: int = 0, idx=None, vals=None,
                with_vals=False, ws=None, stream=None):
-    """Indexer scores and Top-K in one call: same result as topk(index_scores(ix, seq), seq, K, order).
-    method: INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP or INDEX_TOPK_SCORES."""
+    """Indexer scores and Top-K in one call: same result as topk(index_scores(ix, seq), seq, K, order)
+    (order SELECT_PAGES: as topk_pages).  method: INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP or INDEX_TOPK_SCORES."""
     T = seq.num_tokens
     dev = ix.q.device
     if idx is None:

@@ -116,5 +116,33 @@ def tie_band_ok(oracle_scores_row: np.ndarray, K: int, got_ids: np.ndarray, exp_
     return all(abs(float(oracle_scores_row[j]) - sK) <= band for j in diff)
 
 
+def page_max(row):
+    """Largest score of each 64-position page of a row."""
+    n = row.shape[0]
+    return np.array([row[b * 64: b * 64 + 64].max() for b in range((n + 63) // 64)], dtype=np.float32)
+
+
+def page_band_ok(oracle_scores_row, K, got_ids, exp_ids):
+    """Both lists are whole visible pages in ascending order, and the kept page
+    sets differ only in pages whose oracle page score lies within 1e-3 relative
+    of the (K/64)-th best page score."""
+    n = oracle_scores_row.shape[0]
+    for ids in (got_ids, exp_ids):
+        pages = sorted(set(int(x) // 64 for x in ids if x >= 0))
+        whole = [p for b in pages for p in range(b * 64, min(n, b * 64 + 64))]
+        if list(ids[: len(whole)]) != whole or np.any(ids[len(whole):] != -1):
+            return False
+    pm = page_max(oracle_scores_row.astype(np.float64))
+    a = set(int(x) // 64 for x in got_ids if x >= 0)
+    b = set(int(x) // 64 for x in exp_ids if x >= 0)
+    if len(a) != len(b):
+        return False
+    diff = a ^ b
+    if not diff:
+        return True
+    sK = float(np.sort(pm)[::-1][min(K // 64, len(pm)) - 1])
+    return all(abs(float(pm[p]) - sK) <= 1e-3 * abs(sK) for p in diff)
+
+
 def kind_of(wl):
     return wl.cfg["kv_dtype"]

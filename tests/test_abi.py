@@ -151,7 +151,8 @@ def test_index_topk_validation(Lcpu):
                                 ctypes.c_void_p(idx), None, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
     assert f(K=0) == -1
     assert f(K=2049) == -2
-    assert f(order=2) == -1
+    assert f(order=2) == -1                                        # pages: K must be a multiple of 64
+    assert f(order=3) == -1
     assert f(idx=0) == -1
     assert f(ws=0) == -3
     assert f(ws_bytes=need - 1) == -3
@@ -160,6 +161,31 @@ def test_index_topk_validation(Lcpu):
     assert f(method=3) == -1
     assert f(method=-1) == -1
     assert f(method=sia.INDEX_TOPK_ONCHIP, ix=good_indexer(dtype=sia.SIA_F32, heads=4, dim=32)) == -2
+    need64 = L.sia_workspace_size(sia.OP_INDEX_TOPK, ctypes.byref(seq), 64, 1, 1)
+    # the block-aligned selection goes through the score matrix only
+    assert f(K=64, order=sia.SELECT_PAGES, method=sia.INDEX_TOPK_ONCHIP, ws_bytes=need64) == -2
+
+
+def test_topk_pages_validation(Lcpu):
+    L = Lcpu
+    seq = good_seq()
+    need = L.sia_workspace_size(sia.OP_TOPK_PAGES, ctypes.byref(seq), 128, 1, 1)
+    # page scores [4, 4] + last pages [4] + kept pages and their scores [4, 2]
+    assert need >= 4 * 4 * 4 + 4 * 4 + 2 * 4 * 2 * 4
+
+    def f(K=128, idx=FAKE, ws=FAKE, ws_bytes=need, scores=FAKE, ld=256):
+        return L.sia_topk_pages(ctypes.c_void_p(scores), ld, ctypes.byref(seq), K, ctypes.c_void_p(idx), None,
+                                ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    assert f(K=0) == -1
+    assert f(K=100) == -1                                          # not whole pages
+    assert f(K=32) == -1
+    assert f(K=2112) == -2
+    assert f(idx=0) == -1
+    assert f(scores=FAKE + 4) == -1
+    assert f(ld=252) == -1
+    assert f(ws=0) == -3
+    assert f(ws_bytes=need - 1) == -3
+    assert f(ws=FAKE + 64) == -3
 
 
 def test_index_topk_method_choice(Lcpu):
@@ -203,6 +229,7 @@ def test_workspace_size(L):
     n = L.sia_workspace_size(sia.OP_INDEX_SELECT_ATTEND, ctypes.byref(seq), 64, 128, 512)
     assert n >= 4 * 256 * 4 + 4 * 64 * 4
     assert L.sia_workspace_size(sia.OP_TOPK, ctypes.byref(seq), 64, 128, 512) == 0
+    assert L.sia_workspace_size(sia.OP_TOPK_PAGES, ctypes.byref(seq), 64, 128, 512) > 0
     assert L.sia_workspace_size(9, ctypes.byref(seq), 64, 128, 512) == ctypes.c_size_t(-1).value
     bad = good_seq(page_size=16)
     assert L.sia_workspace_size(0, ctypes.byref(bad), 64, 128, 512) == ctypes.c_size_t(-1).value

@@ -16,7 +16,7 @@ import oracle as O
 from sparse_index_attention_amd import sia
 from sparse_index_attention_amd import workloads as W
 
-from gpu_support import check_attention, check_scores, dev, kind_of, tie_band_ok, to_np_out, upload
+from gpu_support import check_attention, check_scores, dev, kind_of, page_band_ok, tie_band_ok, to_np_out, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +126,66 @@ def test_full_size(name):
     check_attention(kind_of(wl), g_out[matched], g_lse[matched], {i: att[int(rows[i])] for i in matched},
                     matched)
     print(f"[full] {name}: ok ({len(matched)}/{len(rows)} rows with identical sets)", flush=True)
+    del seq, ix, q, kv
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+# block-aligned selection at full decode sizes: name -> sampled rows
+PAGE_CASES = {"decode": 4, "quant_decode": 2}
+
+
+@pytest.mark.parametrize("name", list(PAGE_CASES))
+def test_full_size_page_selection(name):
+    print(f"[full-pages] {name}: generating", flush=True)
+    wl = W.make_workload(name)
+    K, H = wl.cfg["K"], wl.cfg["H"]
+    rows = W.sample_rows(wl, PAGE_CASES[name], K)
+    if len(rows) > PAGE_CASES[name]:
+        pick = np.unique(np.linspace(0, len(rows) - 1, PAGE_CASES[name]).round().astype(int))
+        rows = rows[pick]
+    print(f"[full-pages] {name}: sampled rows {list(rows)}", flush=True)
+    seq, ix, q, kv = upload(wl)
+    idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    lse = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+    out = sia.index_select_attend(ix, q, kv, seq, K, wl.softmax_scale, order=sia.SELECT_PAGES, idx_out=idx,
+                                  lse=lse)
+    torch.cuda.synchronize()
+    # every row: whole pages, ascending, -1 trailing, count = visible positions of the kept pages
+    valid = idx >= 0
+    assert bool((valid[:, :-1] | ~valid[:, 1:]).all()), "-1 entries must trail"
+    d = idx[:, 1:] - idx[:, :-1]
+    assert bool(((d > 0) | ~valid[:, 1:]).all()), "positions must ascend"
+    assert bool(((idx <= seq.q_pos.long()[:, None].int()) | ~valid).all()), "index beyond the causal limit"
+    rsel = torch.from_numpy(rows).cuda()
+    g_ids, g_out, g_lse = idx[rsel].cpu().numpy(), to_np_out(out[rsel]), lse[rsel].cpu().numpy()
+    del out, idx, lse
+    torch.cuda.empty_cache()
+
+    print(f"[full-pages] {name}: oracle on {len(rows)} rows", flush=True)
+    ss = sub_seq(seq, wl, rows)
+    sc = O.index_scores(wl.oracle_indexer(), wl.oracle_seq(), [int(t) for t in rows])
+    ld = (wl.max_visible + 3) // 4 * 4
+    buf = np.full((len(rows), ld), np.nan, dtype=np.float32)
+    for i, t in enumerate(rows):
+        buf[i, : sc[int(t)].shape[0]] = sc[int(t)]
+    g_tk = sia.topk_pages(dev(buf), ss, K)
+    torch.cuda.synchronize()
+    g_tk = g_tk.cpu().numpy()
+    sel = {}
+    for i, t in enumerate(rows):
+        sel[int(t)] = O.topk_pages_row(sc[int(t)], K)
+        assert np.array_equal(g_tk[i], sel[int(t)]), f"page selection row {t}"
+    att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), sel, wl.softmax_scale)
+    matched = []
+    for i, t in enumerate(rows):
+        assert page_band_ok(sc[int(t)], K, g_ids[i], sel[int(t)]), f"fused row {t}: pages differ beyond ties"
+        if np.array_equal(g_ids[i], sel[int(t)]):
+            matched.append(i)
+    assert len(matched) >= len(rows) - 1
+    check_attention(kind_of(wl), g_out[matched], g_lse[matched], {i: att[int(rows[i])] for i in matched},
+                    matched)
+    print(f"[full-pages] {name}: ok ({len(matched)}/{len(rows)} rows with identical pages)", flush=True)
     del seq, ix, q, kv
     gc.collect()
     torch.cuda.empty_cache()

@@ -11,8 +11,8 @@ import oracle as O
 from sparse_index_attention_amd import sia
 from sparse_index_attention_amd import workloads as W
 
-from gpu_support import (check_attention, check_scores, dev, kind_of, tie_band_ok, to_np_out, upload,
-                         workload)
+from gpu_support import (check_attention, check_scores, dev, kind_of, page_band_ok, page_max, tie_band_ok,
+                         to_np_out, upload, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -472,3 +472,103 @@ def test_bf16_queries_quantized_in_the_call(name):
     ob = sia.index_select_attend(ix_q, q, kv, seq, K, wl.softmax_scale, idx_out=ib)
     torch.cuda.synchronize()
     assert torch.equal(ia, ib) and torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Block-aligned selection: whole 64-position pages ranked by their best score
+
+def _pages_K(wl):
+    return max(64, wl.cfg["K"] // 64 * 64)
+
+
+@pytest.mark.parametrize("name", TINY)
+def test_topk_pages_bit_exact_on_oracle_scores(name):
+    wl = workload(name)
+    K = _pages_K(wl)
+    print(f"[topk-pages] {name} K={K}", flush=True)
+    seq, _, _, _ = upload(wl)
+    sc, _, _ = oracle_run(name)
+    buf = dev(oracle_score_buffer(wl, sc))          # NaN beyond q_pos: must never be read
+    idx, vals = sia.topk_pages(buf, seq, K, with_vals=True)
+    torch.cuda.synchronize()
+    idx, vals = idx.cpu().numpy(), vals.cpu().numpy()
+    for t in range(wl.Tq):
+        exp = O.topk_pages_row(sc[t], K)
+        assert np.array_equal(idx[t], exp), f"row {t}"
+        m = exp >= 0
+        pm = page_max(sc[t] + np.float32(0))
+        assert np.array_equal(vals[t][m], pm[exp[m] // 64]) and np.all(np.isneginf(vals[t][~m]))
+
+
+@pytest.mark.parametrize("K", [64, 192, 2048])
+def test_topk_pages_edge_rows(K):
+    print(f"[topk-pages-edge] K={K}", flush=True)
+    ns = [1, 2, 63, 64, 65, 127, 128, 129, 1000, 2047, 2048, 2049, 5000, 32768, 12345, 4096, 30000, 777]
+    rows = _synthetic_rows(K + 5, ns)
+    T, mv = len(rows), max(ns)
+    ld = (mv + 3) // 4 * 4
+    buf = np.full((T, ld), np.nan, dtype=np.float32)
+    for t, r in enumerate(rows):
+        buf[t, : len(r)] = r
+    pages = (mv + 63) // 64
+    seq = sia.SeqMap(dev(np.zeros(T, np.int32)), dev(np.array([len(r) - 1 for r in rows], np.int32)),
+                     dev(np.arange(pages, dtype=np.int32)[None]), pages, mv)
+    idx = sia.topk_pages(dev(buf), seq, K)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for t, r in enumerate(rows):
+        assert np.array_equal(idx[t], O.topk_pages_row(r, K)), f"row {t} (n={len(r)})"
+
+
+def test_topk_pages_many_pages():
+    """Rows of up to 600 000 positions (9375 pages): the page Top-K takes its
+    streamed path."""
+    print("[topk-pages-long]", flush=True)
+    ns = [600000, 70000, 1, 4096 * 64 + 3, 123457]
+    rows = _synthetic_rows(7, ns)
+    T, mv = len(rows), max(ns)
+    ld = (mv + 3) // 4 * 4
+    buf = np.full((T, ld), np.nan, dtype=np.float32)
+    for t, r in enumerate(rows):
+        buf[t, : len(r)] = r
+    pages = (mv + 63) // 64
+    seq = sia.SeqMap(dev(np.zeros(T, np.int32)), dev(np.array([len(r) - 1 for r in rows], np.int32)),
+                     dev(np.arange(pages, dtype=np.int32)[None]), pages, mv)
+    idx = sia.topk_pages(dev(buf), seq, 2048)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for t, r in enumerate(rows):
+        assert np.array_equal(idx[t], O.topk_pages_row(r, 2048)), f"row {t} (n={len(r)})"
+
+
+@pytest.mark.parametrize("name", TINY)
+def test_index_topk_and_attend_with_page_selection(name):
+    """sia_index_topk and sia_index_select_attend with SELECT_PAGES: the same
+    ids as scores -> sia_topk_pages on the GPU, the oracle's page selection up
+    to page-score ties, and attention over the oracle's pages."""
+    wl = workload(name)
+    K = _pages_K(wl)
+    print(f"[pages-fused] {name} K={K}", flush=True)
+    seq, ix, q, kv = upload(wl)
+    e_idx = sia.topk_pages(sia.index_scores(ix, seq), seq, K)
+    for m in (sia.INDEX_TOPK_AUTO, sia.INDEX_TOPK_SCORES):
+        g_idx = sia.index_topk(ix, seq, K, order=sia.SELECT_PAGES, method=m)
+        torch.cuda.synchronize()
+        assert torch.equal(g_idx, e_idx), f"method {m}"
+    idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    lse = torch.empty(wl.Tq, wl.cfg["H"], dtype=torch.float32, device="cuda")
+    out = sia.index_select_attend(ix, q, kv, seq, K, wl.softmax_scale, order=sia.SELECT_PAGES, idx_out=idx,
+                                  lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, e_idx)
+    sc, _, _ = oracle_run(name)
+    sel = O.topk_pages(sc, K)
+    ids, o, l = idx.cpu().numpy(), to_np_out(out), lse.cpu().numpy()
+    matched = []
+    for t in range(wl.Tq):
+        assert page_band_ok(sc[t], K, ids[t], sel[t]), f"row {t}: page sets differ beyond the tie band"
+        if np.array_equal(ids[t], sel[t]):
+            matched.append(t)
+    assert len(matched) >= 0.9 * wl.Tq
+    att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), {t: sel[t] for t in matched}, wl.softmax_scale)
+    check_attention(kind_of(wl), o[matched], l[matched], att, matched)
