@@ -37,7 +37,11 @@ def parse():
     p.add_argument("--workload", default="decode",
                    choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill", "mx_decode", "bf16_decode"])
     p.add_argument("--copies", type=int, default=3, help="distinct device copies of the inputs (decode)")
-    p.add_argument("--order", type=int, default=0, help="Top-K output order (0 score-sorted, 1 by position)")
+    p.add_argument("--order", type=int, default=0, choices=[0, 1, 2],
+                   help="selection: Top-K positions score-sorted (0) or by position (1), or whole pages (2)")
+    p.add_argument("--sweep-context", default=None, metavar="C1,C2,...",
+                   help="no headline line: decode step time against context length (decode workloads), one JSON "
+                        "line per context with per-position and page-aligned selection")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-breakdown", action="store_true")
@@ -193,40 +197,22 @@ def cpu_baseline(wl, budget_s):
             "seconds": round(el, 3)}
 
 
-def main():
-    args = parse()
-    if args.traffic:
-        write_traffic(args.workload, *args.traffic)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design note, "
-              "not part of this build.", file=sys.stderr)
-        sys.exit(2)
-
+def dev(x):
     import numpy as np
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def upload_sets(wl, copies):
+    """`copies` distinct device copies of the workload's inputs, each with its
+    own workspace, output and index buffers."""
     import torch
 
     from sparse_index_attention_amd import sia
-    from sparse_index_attention_amd import workloads as W
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    sia.lib()
-    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
-    t_gen = time.perf_counter()
-    wl = W.make_workload(args.workload)
     c = wl.cfg
     K, H = c["K"], c["H"]
-    print(f"[bench] generated in {time.perf_counter() - t_gen:.1f}s; uploading", file=sys.stderr, flush=True)
-
-    def dev(x):
-        if x.dtype == np.uint16:
-            return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-
-    decode = c["kind"] == "decode"
-    copies = max(1, args.copies) if decode else 1
     sets = []
     base = None
     for i in range(copies):
@@ -257,6 +243,114 @@ def main():
         out = torch.empty(wl.Tq, H, c["Dc"], dtype=q.dtype, device="cuda")
         idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
         sets.append(dict(seq=seq, ix=ix, q=q, kv=kv, ws=ws, out=out, idx=idx))
+    torch.cuda.synchronize()
+    return sets
+
+
+def timed_calls(calls, steps, warmup, stream):
+    """Average µs of each (name, fn(i)) over `steps` iterations after `warmup`,
+    from HIP events recorded around every call on the launch stream."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        rec = ev[i - warmup] if i >= warmup else None
+        for k, (_, fn) in enumerate(calls):
+            if rec:
+                rec[k].record(stream)
+            fn(i)
+        if rec:
+            rec[-1].record(stream)
+    torch.cuda.synchronize()
+    return {nm: round(1e3 * sum(r[k].elapsed_time(r[k + 1]) for r in ev) / steps, 2)
+            for k, (nm, _) in enumerate(calls)}
+
+
+def sweep_context(args):
+    """Decode step time against context length (batch and dims of the decode
+    workload), for per-position Top-K and for page-aligned selection."""
+    import torch
+
+    from sparse_index_attention_amd import sia
+    from sparse_index_attention_amd import workloads as W
+    if W.CONFIGS[args.workload]["kind"] != "decode":
+        print("--sweep-context needs a decode workload", file=sys.stderr)
+        sys.exit(2)
+    stream = torch.cuda.current_stream()
+    for ctx in [int(x) for x in args.sweep_context.split(",")]:
+        print(f"[sweep] context {ctx}: generating", file=sys.stderr, flush=True)
+        wl = W.make_workload(args.workload, overrides={"ctx": ctx})
+        c = wl.cfg
+        K, H = c["K"], c["H"]
+        copies = max(1, args.copies)
+        sets = upload_sets(wl, copies)
+        mws = torch.empty(max(sia.workspace_size(sia.OP_MLA_DECODE, sets[0]["seq"], K, H, c["Dc"]), 1),
+                          dtype=torch.uint8, device="cuda")
+        tws = [torch.empty(max(sia.workspace_size(sia.OP_INDEX_TOPK, st["seq"], K, 1, 1), 1), dtype=torch.uint8,
+                           device="cuda") for st in sets]
+        point = {"sweep": "decode_context", "workload": args.workload, "context": ctx,
+                 "batch": int(len(wl.seq_lens)), "K": K, "input_copies": copies}
+        for label, order in (("positions", 0), ("pages", sia.SELECT_PAGES)):
+            def whole(i, order=order):
+                st = sets[i % copies]
+                sia.index_select_attend(st["ix"], st["q"], st["kv"], st["seq"], K, wl.softmax_scale, order=order,
+                                        idx_out=st["idx"], out=st["out"], ws=st["ws"], stream=stream)
+
+            def sel(i, order=order):
+                st = sets[i % copies]
+                sia.index_topk(st["ix"], st["seq"], K, order=order, idx=st["idx"], ws=tws[i % copies],
+                               stream=stream)
+
+            def mla(i):
+                st = sets[i % copies]
+                sia.sparse_mla_decode(st["q"], st["kv"], st["seq"], st["idx"], K, wl.softmax_scale, out=st["out"],
+                                      ws=mws, stream=stream)
+
+            t_step = timed_calls([("step", whole)], args.steps, args.warmup, stream)["step"]
+            parts = timed_calls([("index_topk", sel), ("sparse_mla", mla)], args.steps, args.warmup, stream)
+            point[label] = {"us_per_step": t_step, "query_tokens_per_s": round(wl.Tq / (t_step * 1e-6), 1),
+                            **{k + "_us": v for k, v in parts.items()}}
+        print(json.dumps(point), flush=True)
+        del sets, mws, tws, wl
+        torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    if args.traffic:
+        write_traffic(args.workload, *args.traffic)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design note, "
+              "not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep_context:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        sweep_context(args)
+        return
+
+    import numpy as np
+    import torch
+
+    from sparse_index_attention_amd import sia
+    from sparse_index_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sia.lib()
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    t_gen = time.perf_counter()
+    wl = W.make_workload(args.workload)
+    c = wl.cfg
+    K, H = c["K"], c["H"]
+    print(f"[bench] generated in {time.perf_counter() - t_gen:.1f}s; uploading", file=sys.stderr, flush=True)
+
+    decode = c["kind"] == "decode"
+    copies = max(1, args.copies) if decode else 1
+    sets = upload_sets(wl, copies)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -323,9 +417,15 @@ def main():
             st = sets[i % copies]
             sia.index_scores(st["ix"], st["seq"], scores[i % copies], stream=stream)
 
+        pws = [torch.empty(max(sia.workspace_size(sia.OP_TOPK_PAGES, st["seq"], K, 1, 1), 1), dtype=torch.uint8,
+                           device="cuda") for st in sets] if args.order == sia.SELECT_PAGES else None
+
         def tk(i):
             st = sets[i % copies]
-            sia.topk(scores[i % copies], st["seq"], K, order=args.order, idx=st["idx"], stream=stream)
+            if args.order == sia.SELECT_PAGES:
+                sia.topk_pages(scores[i % copies], st["seq"], K, idx=st["idx"], ws=pws[i % copies], stream=stream)
+            else:
+                sia.topk(scores[i % copies], st["seq"], K, order=args.order, idx=st["idx"], stream=stream)
 
         timed([("index_topk", sel), ("sparse_mla", mla)])
         timed([("index_scores", scr), ("topk", tk)])

@@ -280,9 +280,12 @@ def _seqmap(cfg):
     return q_seq, q_pos, lens, block_table, P
 
 
-def make_workload(name: str, mla=True, indexer=True) -> Workload:
-    """Build the named workload as host (NumPy) arrays."""
+def make_workload(name: str, mla=True, indexer=True, overrides=None) -> Workload:
+    """Build the named workload as host (NumPy) arrays.  `overrides` replaces
+    configuration keys (e.g. {"ctx": 8192} for a decode context sweep); the
+    random streams stay those of the named configuration."""
     cfg = dict(CONFIGS[name])
+    cfg.update(overrides or {})
     cid = cfg["cid"]
     q_seq, q_pos, lens, block_table, P = _seqmap(cfg)
     wl = Workload(name, cfg, q_seq, q_pos, lens, block_table, P)
