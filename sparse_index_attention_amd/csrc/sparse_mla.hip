@@ -161,18 +161,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 128-byte chunk group), and every LDS read is one per-lane base register plus a
 // compile-time immediate.
 //
-// Each workgroup produces one half of the 512 latent output columns (VH = 256).
-// Both halves of a (token, split) recompute the scores S^T; in exchange a wave's
-// output accumulator is 128 registers, which leaves room for the whole query
-// operand in registers and for operand prefetching.  Blocks b and b + 8 (the two
-// halves) are scheduled on the same XCD so the second gather is served by its L2.
+// Work split.  A workgroup takes up to 64 heads of one (token, split): wave
+// (hb, ch) owns head block hb (32 heads) and output column half ch (256 of the
+// 512 latent columns), so its output accumulator is 128 registers.  The two
+// waves of a head block split the score contraction instead of repeating it:
+// wave ch multiplies depth steps 4g + 2ch and 4g + 2ch + 1 (g = 0..8) of the 36
+// 16-deep steps, both write their partial S^T to LDS, and each adds the
+// other's.  Each wave therefore keeps only its half of the query operand in
+// registers (18 steps), and a tile costs a wave 18 + 16 MFMAs.  With 128 heads a
+// (token, split) takes two workgroups; blocks b and b + 8 are those two and are
+// scheduled on the same XCD, so the second gather of the rows is served by its L2.
 constexpr int kVH = 256;
-constexpr int kBufs = 3;                 // gather ring: tiles i+1 and i+2 in flight while i is used
 constexpr int kMaxSplitRows = 2048;      // rows of one split, slots resolved once per workgroup
-// The query operand's first kQReg K-steps stay in registers, the last kQLds are
-// read from LDS (one 16-byte slot per lane and step); this keeps the register
-// allocator from shuffling the operand through AGPRs.
-constexpr int kQLds = 10, kQReg = 36 - kQLds;
+constexpr int kHalfSteps = 18;           // score steps per wave
 constexpr int kVT = kVH / 32;  // 32-column output tiles per half
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt = n (bits 3:0 and 15:14),
@@ -183,6 +184,7 @@ template <int N> __device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amd
 template <int NW, bool FP8>
 __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   constexpr int NT = NW * 64;
+  constexpr int HBW = NW / 2;                  // head blocks per workgroup
   constexpr int TPR = NT / kRowsTile;          // threads per row in the fp8 gather
   constexpr int kFp8Loads = 40 / TPR;          // 640-byte rows = 40 loads of 16 bytes
   // three distinct LDS objects (not one array): the compiler then sees that the
@@ -192,17 +194,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char tile2[kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t sslot[kMaxSplitRows + 2 * kRowsTile];
-  __shared__ __attribute__((aligned(16))) unsigned char qlds[NW * kQLds * 64 * 16];
+  __shared__ __attribute__((aligned(16))) float4 xbuf[NW * 4 * 64];   // partial S^T exchange
 
-  // block -> (token, split, column half); b and b+8 share (token, split)
+  // block -> (token, split, head part); blocks b and b + 8 share (token, split)
+  const int parts = a.H / (32 * HBW);
   const int bid = blockIdx.x;
-  const int grp = bid >> 4, within = bid & 15;
-  const int vhalf = within >> 3;
+  const int grp = bid / (8 * parts), within = bid % (8 * parts);
+  const int part = within >> 3;
   const int unit = grp * 8 + (within & 7);     // token * splits + split
   if (unit >= a.s.T * a.splits) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, nn = lane & 31;
+  const int hbl = wave % HBW, ch = wave / HBW;   // head block in the workgroup, column (and depth) half
+  const int partner = (1 - ch) * HBW + hbl;
   const int split = unit % a.splits;
   const int t = unit / a.splits;
   const int j0 = split * a.rows_per_split;
@@ -213,19 +218,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   const int b = clampi(a.s.q_seq[t], 0, a.s.batch - 1);
   const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
   const int32_t* irow = a.idx + (int64_t)t * a.K;
-  const int head = wave * 32 + nn;
+  const int head = (part * HBW + hbl) * 32 + nn;
   const unsigned char* kvb = (const unsigned char*)a.kv;
-
-  // physical slots of all rows of this split (-1: no row), resolved once
-  for (int r = tid; r < (ntiles + 2) * kRowsTile; r += NT) {
-    const int j = j0 + r;
-    int slot = -1;
-    if (j < j1) {
-      const int p = irow[j];
-      if (p >= 0 && p < a.s.max_visible) slot = (int)page_slot(table, p, a.s.num_pages);
-    }
-    sslot[r] = slot;
-  }
 
   // ---- gather: bf16 rows go global -> LDS directly --------------------------
   // wave instruction (row group rg, chunk group m) covers rows 8rg..8rg+7 and
@@ -313,26 +307,45 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     }
   };
 
-  // ---- query operand: Q^T[depth, head], lane (hh, nn): head nn, chunk 2i + hh
-  v8bf qb[kQReg];
-  lds_u8* const ql = (lds_u8*)qlds + wave * (kQLds * 64 * 16) + lane * 16;
+  // ---- query operand: Q^T[depth, head], lane (hh, nn): head nn.  The wave's
+  // step j is global step st = 4(j/2) + 2ch + j%2, i.e. 16-byte chunk 2st + hh.
+  v8bf qb[kHalfSteps];
   {
     const v8bf* qr = (const v8bf*)((const uint16_t*)a.q + ((int64_t)t * a.H + head) * kD);
 #pragma unroll
-    for (int i = 0; i < kQReg; ++i) qb[i] = qr[2 * i + hh];
-#pragma unroll
-    for (int i = kQReg; i < 36; ++i) *(lds_v8bf*)(ql + (i - kQReg) * 1024) = qr[2 * i + hh];
-    // keep the operand resident: without this the compiler re-loads it from
-    // memory inside the tile loop to save registers
-#pragma unroll
-    for (int i = 0; i < kQReg; ++i) asm volatile("" : "+v"(qb[i]));
+    for (int j = 0; j < kHalfSteps; ++j) qb[j] = qr[2 * (4 * (j >> 1) + 2 * ch + (j & 1)) + hh];
   }
+  // physical slots of all rows of this split (-1: no row), resolved once while
+  // the query loads are in flight: every index load is issued, then every
+  // page-table load, so the split pays two memory latencies, not two per row
+  {
+    constexpr int RMAX = (kMaxSplitRows + 2 * kRowsTile + NT - 1) / NT;
+    const int rows = (ntiles + 2) * kRowsTile;
+    int pos[RMAX];
+#pragma unroll
+    for (int u = 0; u < RMAX; ++u) {
+      const int r = tid + NT * u, j = j0 + r;
+      pos[u] = (r < rows && j < j1) ? irow[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < RMAX; ++u) {
+      const int r = tid + NT * u;
+      const int p = pos[u];
+      const int slot = (p >= 0 && p < a.s.max_visible) ? (int)page_slot(table, p, a.s.num_pages) : -1;
+      if (r < rows) sslot[r] = slot;
+    }
+  }
+  // keep the query operand resident: without this the compiler re-loads it
+  // from memory inside the tile loop to save registers
+#pragma unroll
+  for (int j = 0; j < kHalfSteps; ++j) asm volatile("" : "+v"(qb[j]));
 
   // per-lane LDS read bases (see the layout note above)
-  //  S^T A operand, step st = 4k + mm: chunk 2st + hh -> group k, in-group 2mm + hh
-  int sbase[4];
+  //  S^T A operand, global step st = 4k + mm: chunk 2st + hh -> group k, in-group
+  //  2mm + hh; the wave's steps have mm = 2ch + j%2 and k = j/2
+  int sbase[2];
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) sbase[mm] = 16 * (nn * 8 + ((2 * mm + hh) ^ swz(nn)));
+  for (int x = 0; x < 2; ++x) sbase[x] = 16 * (nn * 8 + ((2 * (2 * ch + x) + hh) ^ swz(nn)));
   //  V^T A operand via transposing reads: source lane s' = lane%16 gives row
   //  offset jrow = s'/4 and vcol quad qd = s'%4; lane group g = lane/16.
   const int g = lane >> 4, sp = lane & 15, jrow = sp >> 2, qd = sp & 3;
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     for (int aa = 0; aa < 2; ++aa) {
       const int vr = vrow0 + 8 * aa;
       vbase[par][aa] = 128 * vr + 16 * ((4 * par + 2 * (g & 1) + (qd >> 1)) ^ swz(vr)) + 8 * (qd & 1) +
-                       4096 * 4 * vhalf;   // column half: chunk groups 4..7
+                       4096 * 4 * ch;      // column half: chunk groups 4..7
     }
 
   // Softmax reference: p = 2^(l - m_ref) with one fixed m_ref per head, the
@@ -403,40 +416,42 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) vflag[k] = *(const int4*)(ss + 8 * k + 4 * hh);
 
-    // S^T = KV . Q^T  (rows x heads): independent accumulation chains (the
-    // MFMA pipeline would otherwise wait out each result), operands loaded PF
-    // steps ahead
-    constexpr int PF = 3, NCH = 1;
-    v16f sch[NCH];
+    // partial S^T = KV . Q^T over this wave's half of the depth (rows x heads),
+    // operands loaded PF steps ahead
+    constexpr int PF = 3;
+    v16f sacc = v16f{};
+    v8bf kring[PF];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) sch[c] = v16f{};
-    v8bf kring[PF], qring[PF];
-    auto qfrag = [&](int st) -> v8bf { return *(lds_v8bf*)(ql + (st - kQReg) * 1024); };
+    for (int j = 0; j < PF; ++j) kring[j] = *(lds_v8bf*)(cur + sbase[j & 1] + 4096 * (j >> 1));
 #pragma unroll
-    for (int st = 0; st < PF; ++st) kring[st] = *(lds_v8bf*)(cur + sbase[st & 3] + 4096 * (st >> 2));
-#pragma unroll
-    for (int st = 0; st < 36; ++st) {
-      const v8bf kf = kring[st % PF];
-      const v8bf qf = st < kQReg ? qb[st < kQReg ? st : 0] : qring[st % PF];
-      if (st + PF < 36) {
-        kring[st % PF] = *(lds_v8bf*)(cur + sbase[(st + PF) & 3] + 4096 * ((st + PF) >> 2));
-        if (st + PF >= kQReg) qring[st % PF] = qfrag(st + PF);
-      }
-      sch[st % NCH] = mfma_bf16(kf, qf, sch[st % NCH]);
+    for (int j = 0; j < kHalfSteps; ++j) {
+      const v8bf kf = kring[j % PF];
+      if (j + PF < kHalfSteps) kring[j % PF] = *(lds_v8bf*)(cur + sbase[(j + PF) & 1] + 4096 * ((j + PF) >> 1));
+      sacc = mfma_bf16(kf, qb[j], sacc);
       // one row load of tile i+1 per step, in the shadow of the MFMAs
       if constexpr (!FP8) {
-        if (st < kRG * 9 && has_next) bstage[st] = *(const v4i*)(nsrc[st / 9] + 128 * (st % 9));
+        if (j < kRG * 9 && has_next) bstage[j] = *(const v4i*)(nsrc[j / 9] + 128 * (j % 9));
       }
       // keep each prefetch PF steps ahead of its use (the scheduler would sink it)
       __builtin_amdgcn_sched_barrier(0);
     }
-    v16f sacc;
+    // exchange the partial sums with the other wave of the head block; both
+    // waves add the same two fp32 values, so both hold the same S^T
+    {
+      float4* mine = xbuf + wave * 256 + lane;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = sch[0][r];
+      for (int k = 0; k < 4; ++k) mine[64 * k] = make_float4(sacc[4 * k], sacc[4 * k + 1], sacc[4 * k + 2], sacc[4 * k + 3]);
+      wait_vm_lgkm0<63>();
+      asm volatile("s_barrier" ::: "memory");
+      const float4* other = xbuf + partner * 256 + lane;
 #pragma unroll
-      for (int c = 1; c < NCH; ++c) acc += sch[c][r];
-      sacc[r] = acc;
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = other[64 * k];
+        sacc[4 * k] += v.x;
+        sacc[4 * k + 1] += v.y;
+        sacc[4 * k + 2] += v.z;
+        sacc[4 * k + 3] += v.w;
+      }
     }
     // online softmax over the tile's rows (log2 domain); lane owns head nn,
     // rows 8*(r/4) + 4*hh + r%4
@@ -517,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  const int vc0 = kVH * vhalf;
+  const int vc0 = kVH * ch;
   if (a.splits == 1) {
     uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + head) * kDc + vc0;
 #pragma unroll
@@ -530,7 +545,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         w.y = pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv);
         *(uint2*)(out + vc) = w;
       }
-    if (a.lse && hh == 0 && vhalf == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
+    if (a.lse && hh == 0 && ch == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
   } else {
     const int64_t pidx = ((int64_t)t * a.splits + split) * a.H + head;
     float* po = a.ws_o + pidx * kDc + vc0;
@@ -542,7 +557,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         *(float4*)(po + vc) = make_float4(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv, o[vt][4 * q4 + 2] * inv,
                                           o[vt][4 * q4 + 3] * inv);
       }
-    if (hh == 0 && vhalf == 0) a.ws_lse[pidx] = lse_v;
+    if (hh == 0 && ch == 0) a.ws_lse[pidx] = lse_v;
   }
 }
 
@@ -587,7 +602,8 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
 int mla_splits(int T, int K, int heads) {
   if (T <= 0) return 1;
   const int cus = num_cus();
-  int s = (cus / 2 + T - 1) / T;         // two column-half workgroups per unit: ~one per CU
+  const int parts = heads >= 128 ? 2 : 1;  // workgroups per (token, split)
+  int s = (cus / parts + T - 1) / T;       // about one workgroup per CU
   const int min_s = (K + kMaxSplitRows - 1) / kMaxSplitRows;   // a split holds at most kMaxSplitRows rows
   const int max_s = (K + kRowsTile * 2 - 1) / (kRowsTile * 2);  // keep >= 2 tiles per split
   s = s > max_s ? max_s : s;
@@ -634,19 +650,20 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
     a.ws_lse = a.ws_o + (size_t)s.T * a.splits * heads * kDc;
   }
   const int64_t units = (int64_t)s.T * a.splits;
-  const dim3 grid((unsigned)(((units + 7) / 8) * 16));
+  const int parts = heads >= 128 ? 2 : 1;
+  const int64_t nblocks = ((units + 7) / 8) * 8 * parts;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nblocks);
   const bool fp8 = kv.dtype == SIA_FP8_E4M3;
 #define SIA_LAUNCH_MLA(NW)                                                                   \
   if (fp8)                                                                                   \
     hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true>), grid, dim3(NW * 64), 0, st, a);        \
   else                                                                                       \
     hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false>), grid, dim3(NW * 64), 0, st, a);
-  if (heads == 128) {
+  if (heads >= 64) {
     SIA_LAUNCH_MLA(4)
-  } else if (heads == 64) {
-    SIA_LAUNCH_MLA(2)
   } else {
-    SIA_LAUNCH_MLA(1)
+    SIA_LAUNCH_MLA(2)
   }
 #undef SIA_LAUNCH_MLA
   hipError_t e = hipGetLastError();
