@@ -194,7 +194,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char tile2[kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t sslot[kMaxSplitRows + 2 * kRowsTile];
-  __shared__ __attribute__((aligned(16))) float4 xbuf[NW * 4 * 64];   // partial S^T exchange
+  __shared__ __attribute__((aligned(16))) float smask[FP8 ? 4 : kMaxSplitRows + 2 * kRowsTile];  // 0 or -inf per row
+  __shared__ __attribute__((aligned(16))) float4 xbuf[2 * NW * 4 * 64];   // partial S^T exchange, two parities
 
   // block -> (token, split, head part); blocks b and b + 8 share (token, split)
   const int parts = a.H / (32 * HBW);
@@ -260,6 +261,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         *(lds_v4i*)(dst + 4096 * m + 1024 * (wave + NW * k) + 16 * lane) = bstage[k * 9 + m];
   };
 
+  // the same rows straight into LDS (bf16 pipeline below): one wave instruction
+  // fills the 64 consecutive 16-byte slots of (row group, chunk group)
+  auto issue_dma = [&](int i, lds_u8* dst) __attribute__((always_inline)) {
+    const int32_t* ss = sslot + i * kRowsTile;
+#pragma unroll
+    for (int k = 0; k < kRG; ++k) {
+      const int r = 8 * (wave + NW * k) + (lane >> 3);
+      const int slot = ss[r] >= 0 ? ss[r] : 0;
+      const unsigned char* src = kvb + (int64_t)slot * (kD * 2) + 16 * (g_sub ^ swz(r));
+#pragma unroll
+      for (int m = 0; m < 9; ++m)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 128 * m),
+                                         (lds_void*)(dst + 4096 * m + 1024 * (wave + NW * k)), 16, 0, 0);
+    }
+  };
+
   // ---- gather: fp8 rows go through registers and are dequantized to bf16 ----
   // thread -> row tid / TPR, 16-byte source chunks c = tid % TPR + TPR * m
   v4i stage[FP8 ? kFp8Loads : 1];
@@ -321,18 +338,26 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   {
     constexpr int RMAX = (kMaxSplitRows + 2 * kRowsTile + NT - 1) / NT;
     const int rows = (ntiles + 2) * kRowsTile;
+    // loads are unconditional (clamped indices) so that none waits for another
     int pos[RMAX];
 #pragma unroll
     for (int u = 0; u < RMAX; ++u) {
-      const int r = tid + NT * u, j = j0 + r;
-      pos[u] = (r < rows && j < j1) ? irow[j] : -1;
+      const int j = j0 + tid + NT * u;
+      pos[u] = irow[j < a.K ? j : a.K - 1];
+    }
+    int page[RMAX];
+#pragma unroll
+    for (int u = 0; u < RMAX; ++u) {
+      const int p = pos[u];
+      page[u] = table[(p >= 0 && p < a.s.max_visible ? p : 0) >> 6];
     }
 #pragma unroll
     for (int u = 0; u < RMAX; ++u) {
-      const int r = tid + NT * u;
-      const int p = pos[u];
-      const int slot = (p >= 0 && p < a.s.max_visible) ? (int)page_slot(table, p, a.s.num_pages) : -1;
-      if (r < rows) sslot[r] = slot;
+      const int r = tid + NT * u, p = pos[u];
+      const bool ok = r < rows && j0 + r < j1 && p >= 0 && p < a.s.max_visible;
+      const int pg = clampi(page[u], 0, a.s.num_pages - 1);
+      if (r < rows) sslot[r] = ok ? pg * kPage + (p & (kPage - 1)) : -1;
+      if (!FP8 && r < rows) smask[r] = ok ? 0.f : -INFINITY;
     }
   }
   // keep the query operand resident: without this the compiler re-loads it
@@ -375,6 +400,176 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   lds_u8* const T1 = (lds_u8*)tile1;
   lds_u8* const T2 = (lds_u8*)tile2;
   __syncthreads();
+  if constexpr (!FP8) {
+  // ---- bf16: software-pipelined tiles ------------------------------------
+  // Iteration i requests tile i+2 into the buffer tile i-1 used, computes the
+  // partial scores of tile i+1 while the softmax of tile i runs between its
+  // MFMAs, then O += V^T P^T for tile i, and ends with the one barrier that
+  // publishes tile i+2 and the partial scores of tile i+1.  Requests and score
+  // passes past the last tile run on the slot table's -1 padding (slot 0) and
+  // their results are never used; this keeps the loop free of conditional
+  // requests, which would make the compiler drain every load before each read.
+  // additive masks of this lane's 16 rows of tile i (rows 8k + 4hh + 0..3
+  // are four consecutive entries)
+  struct Flags {
+    float4 f[4];
+  };
+  auto load_flags = [&](int i) __attribute__((always_inline)) -> Flags {
+    const float* sm = smask + i * kRowsTile;
+    Flags fl;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fl.f[k] = *(const float4*)(sm + 8 * k + 4 * hh);
+    return fl;
+  };
+  // operands are read PF steps ahead of their MFMA: LDS latency is about six
+  // MFMA issue slots
+  constexpr int PF = 6, PFV = 6;
+  // partial S^T of the tile in `buf` over this wave's half of the depth;
+  // between(j) runs after the MFMA of step j
+  auto s_partial = [&](lds_u8* buf, auto&& between) __attribute__((always_inline)) -> v16f {
+    v16f acc = v16f{};
+    v8bf kring[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) kring[j] = *(lds_v8bf*)(buf + sbase[j & 1] + 4096 * (j >> 1));
+#pragma unroll
+    for (int j = 0; j < kHalfSteps; ++j) {
+      const v8bf kf = kring[j % PF];
+      if (j + PF < kHalfSteps) kring[j % PF] = *(lds_v8bf*)(buf + sbase[(j + PF) & 1] + 4096 * ((j + PF) >> 1));
+      acc = mfma_bf16(kf, qb[j], acc);
+      between(j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+  auto xwrite = [&](const v16f& acc, int par) __attribute__((always_inline)) {
+    float4* mine = xbuf + (par * NW + wave) * 256 + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mine[64 * k] = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
+  };
+  // both waves of a head block add the same two fp32 values: identical S^T
+  auto xadd = [&](v16f& acc, int par) __attribute__((always_inline)) {
+    const float4* other = xbuf + (par * NW + partner) * 256 + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = other[64 * k];
+      acc[4 * k] += v.x;
+      acc[4 * k + 1] += v.y;
+      acc[4 * k + 2] += v.z;
+      acc[4 * k + 3] += v.w;
+    }
+  };
+  v16f sacc;   // full S^T of the tile the next iteration finishes
+  // gather of tile i+2 spread over the score steps: source rows first, then
+  // one 16-byte request per lane and step
+  auto dma_src = [&](int i, int k) __attribute__((always_inline)) -> const unsigned char* {
+    const int r = 8 * (wave + NW * k) + (lane >> 3);
+    const int slot = sslot[i * kRowsTile + r];
+    return kvb + (int64_t)(slot >= 0 ? slot : 0) * (kD * 2) + 16 * (g_sub ^ swz(r));
+  };
+  auto dma_one = [&](const unsigned char* src, lds_u8* dst, int k, int m) __attribute__((always_inline)) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 128 * m),
+                                     (lds_void*)(dst + 4096 * m + 1024 * (wave + NW * k)), 16, 0, 0);
+  };
+  auto iter = [&](int i, lds_u8* cur, lds_u8* nxt, lds_u8* fut) __attribute__((always_inline)) {
+    const unsigned char* dsrc[kRG];
+#pragma unroll
+    for (int k = 0; k < kRG; ++k) dsrc[k] = dma_src(i + 2, k);
+    const Flags fl = load_flags(i);
+    // softmax of tile i (log2 domain; lane owns head nn, rows 8(r/4) + 4hh + r%4).
+    // The maximum over both lane halves (one v_permlane32_swap) is needed only
+    // until m_ref is set; afterwards each lane tracks its own maximum, for the
+    // overflow test and the second pass, and p = 2^(s * scale - m_ref) is one
+    // FMA and one exp (invalid rows hold -inf and give 0).
+    float sv[16];
+    float tloc = -INFINITY, psum = 0.f, mneg = 0.f;
+    v8bf pb[2];
+    auto soft = [&](int j) __attribute__((always_inline)) {
+      if (j < kRG * 9) dma_one(dsrc[j / 9], fut, j / 9, j % 9);
+      if (j == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float4 f = fl.f[r >> 2];
+          sv[r] = sacc[r] + ((r & 3) == 0 ? f.x : (r & 3) == 1 ? f.y : (r & 3) == 2 ? f.z : f.w);
+          tloc = fmaxf(tloc, sv[r]);
+        }
+      } else if (j == 1) {
+        tloc *= a.scale_log2;  // the scale is positive
+        m_seen = fmaxf(m_seen, tloc);
+        if (__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tloc), __float_as_uint(tloc), false, false);
+          const float both = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          if (m_ref == -INFINITY) m_ref = both;
+        }
+        overflow |= tloc > m_ref + 100.f;
+        mneg = m_ref == -INFINITY ? -INFINITY : -m_ref;   // no valid row yet: every p is 0
+      } else if (j < 10) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = 2 * (j - 2) + rr;
+          const float pv = fast_exp2(fmaf(sv[r], a.scale_log2, mneg));
+          psum += pv;
+          pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
+        }
+      }
+    };
+    v16f snext = s_partial(nxt, soft);
+    xwrite(snext, (i + 1) & 1);
+    // O^T += V^T . P^T for tile i; MFMA mf covers tile rows 16mf + R(hh, jj)
+    auto vfrag = [&](int vt, int mf) -> v8bf {
+      const int imm = 4096 * (vt >> 1) + 2048 * mf;
+      const v4bf x0 = lds_tr16(cur, vbase[vt & 1][0] + imm);
+      const v4bf x1 = lds_tr16(cur, vbase[vt & 1][1] + imm);
+      return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    v8bf vring[PFV];
+#pragma unroll
+    for (int k = 0; k < PFV; ++k) vring[k] = vfrag(k % kVT, k / kVT);
+#pragma unroll
+    for (int k = 0; k < 2 * kVT; ++k) {
+      const int vt = k % kVT, mf = k / kVT;
+      const v8bf af = vring[k % PFV];
+      if (k + PFV < 2 * kVT) vring[k % PFV] = vfrag((k + PFV) % kVT, (k + PFV) / kVT);
+      o[vt] = mfma_bf16(af, pb[mf], o[vt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += psum;
+    // tile i+2 is in LDS and the partial scores of tile i+1 are published
+    wait_vm_lgkm0<0>();
+    asm volatile("s_barrier" ::: "memory");
+    xadd(snext, (i + 1) & 1);
+    sacc = snext;
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int v = 0; v < kVT; ++v) o[v] = v16f{};
+    l_run = 0.f;
+    overflow = false;
+    if (pass == 1) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m_seen), __float_as_uint(m_seen), false, false);
+      m_ref = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // prologue: tiles 0 and 1 in LDS, full scores of tile 0
+    issue_dma(0, T0);
+    issue_dma(1, T1);
+    wait_vm_lgkm0<0>();
+    asm volatile("s_barrier" ::: "memory");
+    sacc = s_partial(T0, [](int) {});
+    xwrite(sacc, 0);
+    wait_vm_lgkm0<63>();
+    asm volatile("s_barrier" ::: "memory");
+    xadd(sacc, 0);
+    int i = 0;
+    for (; i + 3 <= ntiles; i += 3) {
+      iter(i, T0, T1, T2);
+      iter(i + 1, T1, T2, T0);
+      iter(i + 2, T2, T0, T1);
+    }
+    if (i < ntiles) iter(i, T0, T1, T2);
+    if (i + 1 < ntiles) iter(i + 1, T1, T2, T0);
+    // every wave agrees on a second pass; the barrier also retires this pass's tiles
+    if (!__syncthreads_or(overflow)) break;
+  }
+  } else {
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
   for (int v = 0; v < kVT; ++v) o[v] = v16f{};
@@ -526,6 +721,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   if (i + 1 < ntiles) tile_step(i + 1, T1, T2, T0);
   // every wave agrees on a second pass; the barrier also retires this pass's tiles
   if (!__syncthreads_or(overflow)) break;
+  }
   }
 
   // ---- finish: normalise and write this column half
