@@ -276,6 +276,10 @@ int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dty
 size_t sia_workspace_size(int32_t op, const sia_seqmap* seq, int32_t K, int32_t heads,
                           int32_t latent_dim);
 
+/* Empty batches: with seq->num_tokens == 0 every compute entry point returns
+ * SIA_OK without launching anything once the scalar arguments (K, order,
+ * method, dtypes and shapes) are valid; data pointers may then be NULL.       */
+
 /* Static text for a sia_status value. */
 const char* sia_status_string(int status);
 

@@ -39,22 +39,26 @@ static int check_seq(const sia_seqmap* s) {
   return SIA_OK;
 }
 
-static int check_indexer(const sia_indexer_in* in) {
-  if (!in || !in->q || !in->w || !in->k_pool) return SIA_ERR_INVALID_ARG;
+// Shapes and dtypes always; pointers and their alignment only when there is
+// work (num_tokens > 0).
+static int check_indexer(const sia_indexer_in* in, int num_tokens = 1) {
+  if (!in) return SIA_ERR_INVALID_ARG;
   if (in->heads < 1 || in->dim < 1) return SIA_ERR_INVALID_ARG;
+  const bool data = num_tokens > 0;
+  if (data && (!in->q || !in->w || !in->k_pool)) return SIA_ERR_INVALID_ARG;
   if (in->q_bf16 != 0 && in->q_bf16 != 1) return SIA_ERR_INVALID_ARG;
   if (in->dtype == SIA_BF16) {
     if (in->q_bf16) return SIA_ERR_UNSUPPORTED;   // q already bfloat16
     if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
-    if (!aligned16(in->q) || !aligned16(in->k_pool)) return SIA_ERR_INVALID_ARG;
+    if (data && (!aligned16(in->q) || !aligned16(in->k_pool))) return SIA_ERR_INVALID_ARG;
   } else if (in->dtype == SIA_F32) {
     if (in->q_bf16) return SIA_ERR_UNSUPPORTED;
     if (in->heads > 64 || (int64_t)in->heads * in->dim > 4096) return SIA_ERR_UNSUPPORTED;
   } else if (in->dtype == SIA_FP8_E4M3 || in->dtype == SIA_MXFP8_E4M3) {
-    if ((!in->q_bf16 && !in->q_scale) || !in->k_scale) return SIA_ERR_INVALID_ARG;
+    if (data && ((!in->q_bf16 && !in->q_scale) || !in->k_scale)) return SIA_ERR_INVALID_ARG;
     if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
-    if (!aligned16(in->q) || !aligned16(in->k_pool)) return SIA_ERR_INVALID_ARG;
-    if (in->dtype == SIA_MXFP8_E4M3 &&
+    if (data && (!aligned16(in->q) || !aligned16(in->k_pool))) return SIA_ERR_INVALID_ARG;
+    if (data && in->dtype == SIA_MXFP8_E4M3 &&
         ((!in->q_bf16 && (reinterpret_cast<uintptr_t>(in->q_scale) & 3u)) ||
          (reinterpret_cast<uintptr_t>(in->k_scale) & 3u)))
       return SIA_ERR_INVALID_ARG;
@@ -65,6 +69,7 @@ static int check_indexer(const sia_indexer_in* in) {
 }
 
 static int check_scores(const float* scores, int64_t ld, const sia_seqmap* s) {
+  if (s->num_tokens == 0) return SIA_OK;   // nothing is read
   if (!scores || !aligned16(scores)) return SIA_ERR_INVALID_ARG;
   if (ld < 1 || (ld & 3) != 0) return SIA_ERR_INVALID_ARG;
   if (s->num_tokens > 0 && ld < s->max_visible) return SIA_ERR_INVALID_ARG;
@@ -207,7 +212,7 @@ int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* sco
                      hipStream_t stream) {
   int rc = check_seq(seq);
   if (rc) return rc;
-  rc = check_indexer(in);
+  rc = check_indexer(in, seq->num_tokens);
   if (rc) return rc;
   rc = check_scores(scores, ld, seq);
   if (rc) return rc;
@@ -222,7 +227,9 @@ int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, 
   if (rc) return rc;
   rc = check_scores(scores, ld, seq);
   if (rc) return rc;
-  if (K < 1 || K > 2048 || (order != 0 && order != 1) || !idx) return K > 2048 ? SIA_ERR_UNSUPPORTED : SIA_ERR_INVALID_ARG;
+  if (K < 1 || K > 2048 || (order != 0 && order != 1)) return K > 2048 ? SIA_ERR_UNSUPPORTED : SIA_ERR_INVALID_ARG;
+  if (seq->num_tokens == 0) return SIA_OK;
+  if (!idx) return SIA_ERR_INVALID_ARG;
   const hipError_t e = launch_topk(scores, ld, seq_args(*seq), K, order, idx, vals, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);
 }
@@ -233,10 +240,10 @@ int sia_topk_pages(const float* scores, int64_t ld, const sia_seqmap* seq, int32
   if (rc) return rc;
   rc = check_scores(scores, ld, seq);
   if (rc) return rc;
-  if (!idx) return SIA_ERR_INVALID_ARG;
   rc = check_select(K, SIA_SELECT_PAGES);
   if (rc) return rc;
   if (seq->num_tokens == 0) return SIA_OK;
+  if (!idx) return SIA_ERR_INVALID_ARG;
   const size_t need = sia_workspace_size(SIA_OP_TOPK_PAGES, seq, K, 1, 1);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
   const hipError_t e = launch_topk_pages(scores, ld, seq_args(*seq), K, idx, vals, ws, stream);
@@ -300,9 +307,8 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
                    int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_seq(seq);
   if (rc) return rc;
-  rc = check_indexer(in);
+  rc = check_indexer(in, seq->num_tokens);
   if (rc) return rc;
-  if (!idx) return SIA_ERR_INVALID_ARG;
   if (method < SIA_INDEX_TOPK_AUTO || method > SIA_INDEX_TOPK_SCORES) return SIA_ERR_INVALID_ARG;
   rc = check_select(K, order);
   if (rc) return rc;
@@ -310,6 +316,7 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
       ((in->dtype != SIA_FP8_E4M3 && in->dtype != SIA_MXFP8_E4M3) || order == SIA_SELECT_PAGES))
     return SIA_ERR_UNSUPPORTED;
   if (seq->num_tokens == 0) return SIA_OK;
+  if (!idx) return SIA_ERR_INVALID_ARG;
   const size_t need = sia_workspace_size(SIA_OP_INDEX_TOPK, seq, K, 1, 1);
   if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return SIA_ERR_WORKSPACE;
   if (method == SIA_INDEX_TOPK_AUTO)
@@ -333,7 +340,7 @@ int sia_quantize_indexer_q(const sia_indexer_in* in, int32_t num_tokens, void* q
 int sia_index_topk_method(const sia_indexer_in* in, const sia_seqmap* seq) {
   int rc = check_seq(seq);
   if (rc) return rc;
-  rc = check_indexer(in);
+  rc = check_indexer(in, seq->num_tokens);
   if (rc) return rc;
   return index_topk_auto(*in, *seq);
 }
@@ -344,7 +351,7 @@ int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dty
                             size_t ws_bytes, hipStream_t stream) {
   int rc = check_seq(seq);
   if (rc) return rc;
-  rc = check_indexer(in);
+  rc = check_indexer(in, seq->num_tokens);
   if (rc) return rc;
   rc = check_select(K, order);
   if (rc) return rc;

@@ -572,3 +572,45 @@ def test_index_topk_and_attend_with_page_selection(name):
     assert len(matched) >= 0.9 * wl.Tq
     att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), {t: sel[t] for t in matched}, wl.softmax_scale)
     check_attention(kind_of(wl), o[matched], l[matched], att, matched)
+
+
+@pytest.mark.parametrize("name", ["decode_tiny", "quant_decode_tiny", "decode_h64_tiny", "tiny_prefill"])
+@pytest.mark.parametrize("K", [1, 33, 100])
+def test_sparse_mla_ragged_row_counts(name, K):
+    """Index lists whose length is not a multiple of the 32-row tile (a
+    partial last tile, and a single row), both entry points."""
+    wl = workload(name)
+    print(f"[mla-ragged] {name} K={K}", flush=True)
+    sc, _, _ = oracle_run(name)
+    sel = {t: O.topk_row(sc[t], K, 0) for t in range(wl.Tq)}
+    ids = np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32)
+    att = O.sparse_mla(wl.q, wl.oracle_kv(), wl.oracle_seq(), sel, wl.softmax_scale)
+    seq, _, q, kv = upload(wl)
+    lse = torch.empty(wl.Tq, wl.cfg["H"], dtype=torch.float32, device="cuda")
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        out = fn(q, kv, seq, dev(ids), K, wl.softmax_scale, lse=lse)
+        torch.cuda.synchronize()
+        check_attention(kind_of(wl), to_np_out(out), lse.cpu().numpy(), att, range(wl.Tq))
+
+
+def test_zero_token_calls_are_noops():
+    """Every entry point accepts an empty batch on real device buffers and
+    leaves its outputs untouched."""
+    print("[zero-tokens]", flush=True)
+    wl = workload("decode_tiny")
+    seq_full, ix, q, kv = upload(wl)
+    empty_i = torch.empty(0, dtype=torch.int32, device="cuda")
+    seq = sia.SeqMap(empty_i, empty_i, seq_full.block_table, seq_full.num_pages, seq_full.max_visible)
+    K = wl.cfg["K"]
+    ix0 = sia.Indexer(ix.q[:0], ix.w[:0], ix.k_pool, ix.q_scale[:0], ix.k_scale)
+    sentinel = torch.full((1, 8), 7.0, device="cuda")
+    sc = sia.index_scores(ix0, seq, scores=sentinel, ld=8)
+    assert sc.shape[0] == 1 and bool((sentinel == 7.0).all())
+    assert sia.topk(sentinel, seq, K).shape == (0, K)
+    assert sia.topk_pages(sentinel, seq, 64).shape == (0, 64)
+    assert sia.index_topk(ix0, seq, K).shape == (0, K)
+    out = sia.sparse_mla_decode(q[:0], kv, seq, empty_i.view(0, 1).expand(0, K).contiguous(), K, wl.softmax_scale)
+    assert out.shape[0] == 0
+    out = sia.index_select_attend(ix0, q[:0], kv, seq, K, wl.softmax_scale)
+    assert out.shape[0] == 0
+    torch.cuda.synchronize()
