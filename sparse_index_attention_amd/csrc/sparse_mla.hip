@@ -758,40 +758,62 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, in split order.
-template <bool F32OUT>
+// One wave per (token, head), eight output columns per lane.  Every load of a
+// group of kCombineGroup splits is issued before the first result is used (the
+// split LSEs lane-parallel, one split per lane), so a merge of up to four
+// splits waits on memory once instead of twice per split.
+constexpr int kCombineGroup = 4;
+constexpr int kMaxSplits = 32;  // mla_splits never returns more; one LSE per lane
+
 __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
   const int t = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (h >= a.H) return;
-  const int S = a.splits, Dc = a.Dc;
-  float mx = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, a.ws_lse[((int64_t)t * S + sp) * a.H + h]);
+  const int S = a.splits;
+  const int64_t hstride = (int64_t)a.H * kDc;  // between the partials of consecutive splits
+  const float* __restrict__ lse_t = a.ws_lse + (int64_t)t * S * a.H + h;
+  const float* __restrict__ o_t = a.ws_o + ((int64_t)t * S * a.H + h) * kDc + lane * 8;
+
+  const float ls = lane < S ? lse_t[(int64_t)lane * a.H] : -INFINITY;
+  float4 v[kCombineGroup][2];
+  auto load_group = [&](int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u)
+      if (g + u < S) {
+        const float4* po = reinterpret_cast<const float4*>(o_t + (g + u) * hstride);
+        v[u][0] = po[0];
+        v[u][1] = po[1];
+      }
+  };
+  load_group(0);
+  const float mx = wave_max(ls);  // exact, so every lane holds the same value
+  const float wl = mx == -INFINITY ? 0.f : __expf(ls - mx);
+
   float tot = 0.f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int sp = 0; sp < S; ++sp) {
-    const int64_t pidx = ((int64_t)t * S + sp) * a.H + h;
-    const float ls = a.ws_lse[pidx];
-    const float wgt = (mx == -INFINITY) ? 0.f : __expf(ls - mx);
-    tot += wgt;
-    if (wgt != 0.f) {
-      const float* po = a.ws_o + pidx * Dc;
-      for (int d = lane * 8, k = 0; k < 8; ++k) acc[k] = fmaf(wgt, po[d + k], acc[k]);
+  for (int g = 0; g < S; g += kCombineGroup) {
+    if (g > 0) load_group(g);
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      if (g + u >= S) break;
+      const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), g + u));
+      tot += wgt;
+      if (wgt != 0.f) {
+        const float x[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = fmaf(wgt, x[k], acc[k]);
+      }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  if (F32OUT) {
-    float* out = (float*)a.out + ((int64_t)t * a.H + h) * Dc + lane * 8;
-    for (int k = 0; k < 8; ++k) out[k] = acc[k] * inv;
-  } else {
-    uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + h) * Dc + lane * 8;
-    uint4 w;
-    w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-    w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-    *(uint4*)out = w;
-  }
+  uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + h) * kDc + lane * 8;
+  uint4 w;
+  w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *(uint4*)out = w;
   if (a.lse && lane == 0) a.lse[(int64_t)t * a.H + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
 }
 
@@ -803,7 +825,7 @@ int mla_splits(int T, int K, int heads) {
   const int min_s = (K + kMaxSplitRows - 1) / kMaxSplitRows;   // a split holds at most kMaxSplitRows rows
   const int max_s = (K + kRowsTile * 2 - 1) / (kRowsTile * 2);  // keep >= 2 tiles per split
   s = s > max_s ? max_s : s;
-  s = s > 32 ? 32 : s;
+  s = s > kMaxSplits ? kMaxSplits : s;
   s = s < min_s ? min_s : s;
   return s < 1 ? 1 : s;
 }
@@ -838,6 +860,7 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
     return hipGetLastError();
   }
   a.splits = splits < 1 ? 1 : splits;
+  if (a.splits > kMaxSplits) return hipErrorInvalidValue;
   int rps = (K + a.splits - 1) / a.splits;
   rps = (rps + kRowsTile - 1) / kRowsTile * kRowsTile;
   a.rows_per_split = rps;
@@ -864,7 +887,7 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
 #undef SIA_LAUNCH_MLA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(k_mla_combine<false>, dim3(s.T, (heads + 3) / 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_mla_combine, dim3(s.T, (heads + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
