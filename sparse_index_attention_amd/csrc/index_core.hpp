@@ -68,16 +68,18 @@ __device__ __forceinline__ v8i mx_operand(const uint8_t* row, int hh) {
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// One wave scores query t against the 64-key pages [c_begin, c_end) of its
-// sequence's block table and calls sink(s, score) once per page with lane l
-// holding key s = 64c + l (scores of keys past pos are -inf).
+// One wave scores query t against 64-key pages of its sequence's block table
+// and calls sink(s, score) once per page with lane l holding key s = 64c + l
+// (scores of keys past pos are -inf).  The pages are c = claim(), claim(), ...
+// until claim() returns -1; claim() must return a wave-uniform value and, once
+// it has returned -1, keep doing so.
 // Lane l: nn = l % 32 (key within an N tile / head within an M tile), hh = l / 32.
 // K-step mapping (same for both operands): step st of lane half hh covers
 // depth bytes [64*hh + 32*st, 64*hh + 32*st + 32).
 // MX: MXFP8 inputs (group scales inside the MFMA; no per-token scales).
-template <int HI, bool MX, typename Sink>
-__device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, int b, int c_begin, int c_end,
-                                            Sink&& sink) {
+template <int HI, bool MX, typename Claim, typename Sink>
+__device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, int pos, int b, Claim&& claim,
+                                                    Sink&& sink) {
   constexpr int MT = HI / 32;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5, nn = lane & 31;
@@ -117,9 +119,13 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
   };
   v8i k0[2][2], k1[2][2], k2[2][2];
   KScale ks0{}, ks1{}, ks2{};
-  load_page(c_begin, k0, ks0);
-  if (c_begin + 1 < c_end) load_page(c_begin + 1, k1, ks1);
-  if (c_begin + 2 < c_end) load_page(c_begin + 2, k2, ks2);
+  int c0 = claim();
+  if (c0 < 0) return;
+  load_page(c0, k0, ks0);
+  int c1 = claim();
+  if (c1 >= 0) load_page(c1, k1, ks1);
+  int c2 = claim();
+  if (c2 >= 0) load_page(c2, k2, ks2);
 
   // query operand (A): head m = 32*mt + nn
   v8i qa[MT][2];
@@ -144,8 +150,9 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
       wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
     }
   }
-  // scores of page c from buffer kb, then buffer kb takes page c+3
-  auto step = [&](int c, v8i (&kb)[2][2], KScale& ks) __attribute__((always_inline)) {
+  // scores of page c from buffer kb, then buffer kb takes the next claimed
+  // page (returned; -1 when none is left)
+  auto step = [&](int c, v8i (&kb)[2][2], KScale& ks) __attribute__((always_inline)) -> int {
     float p[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -177,16 +184,28 @@ __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, 
     const int s = c * 64 + lane;
     if (s > pos) score = -INFINITY;
     sink(s, score);
-    if (c + 3 < c_end) load_page(c + 3, kb, ks);
+    const int next = claim();
+    if (next >= 0) load_page(next, kb, ks);
+    return next;
   };
-  int c = c_begin;
-  for (; c + 3 <= c_end; c += 3) {
-    step(c, k0, ks0);
-    step(c + 1, k1, ks1);
-    step(c + 2, k2, ks2);
+  // pages are claimed in processing order, so the first -1 ends the ring
+  while (true) {
+    c0 = step(c0, k0, ks0);
+    if (c1 < 0) break;
+    c1 = step(c1, k1, ks1);
+    if (c2 < 0) break;
+    c2 = step(c2, k2, ks2);
+    if (c0 < 0) break;
   }
-  if (c < c_end) step(c, k0, ks0);
-  if (c + 1 < c_end) step(c + 1, k1, ks1);
+}
+
+// The pages [c_begin, c_end) in order.
+template <int HI, bool MX, typename Sink>
+__device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, int b, int c_begin, int c_end,
+                                            Sink&& sink) {
+  int next = c_begin;
+  score_claimed_pages<HI, MX>(a, t, pos, b, [&]() __attribute__((always_inline)) { return next < c_end ? next++ : -1; },
+                              sink);
 }
 
 }  // namespace sia

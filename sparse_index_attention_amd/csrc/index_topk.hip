@@ -33,13 +33,18 @@ constexpr int kRNT = 512;
 constexpr int kRNW = kRNT / 64;
 constexpr int kRPer = kIndexTopkRangeKeys / kRNT;          // keys per thread: 16
 constexpr int kRBins = 2048;
+constexpr int kRList = kRNT;
+static_assert(2 * kMaxTopK <= kIndexTopkRangeKeys, "output staging reuses the score buffer");  // threshold-bin keys ranked by brute force (one per thread)
 
 struct RangeSmem {
-  float sc[kIndexTopkRangeKeys];
+  float sc[kIndexTopkRangeKeys];  // scores; after the keys are in registers, the output staging
   uint32_t hist[kRBins];
+  uint32_t lkey[kRList];
+  int32_t lpos[kRList];
   uint32_t red[2][kRNW];
   uint32_t scan[2][kRNW];
-  uint32_t found_bin, found_above;
+  uint32_t found_bin, found_above, found_cnt, list_n, found_key, found_need;
+  uint32_t next_page;  // pages of the range claimed so far
 };
 
 template <int HI, bool MX>
@@ -62,23 +67,35 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
   const int nr = n - key0 < kIndexTopkRangeKeys ? n - key0 : kIndexTopkRangeKeys;
   const int b = clampi(a.s.q_seq[t], 0, a.s.batch - 1);
 
-  // ---- 1. scores of the range into LDS: wave w takes pages c0 + 16w ...
-  {
-    const int cb = c0 + 16 * w;
-    const int ce = cb + 16 < c1 ? cb + 16 : c1;
-    if (cb < ce)
-      score_pages<HI, MX>(a, t, pos, b, cb, ce, [&](int s, float score) __attribute__((always_inline)) {
-        sh.sc[s - key0] = score;
-      });
-  }
+  // ---- 1. scores of the range into LDS.  The waves claim pages one at a
+  // time from a shared counter: with a fixed share each, the slowest wave's
+  // memory latency would hold up the whole workgroup at the barrier.
+  if (tid == 0) sh.next_page = 0;
+  __syncthreads();
+  score_claimed_pages<HI, MX>(
+      a, t, pos, b,
+      [&]() __attribute__((always_inline)) -> int {
+        uint32_t v = 0;
+        if (lane == 0) v = atomicAdd(&sh.next_page, 1u);
+        const int c = c0 + __builtin_amdgcn_readfirstlane((int)v);
+        return c < c1 ? c : -1;
+      },
+      [&](int s, float score) __attribute__((always_inline)) { sh.sc[s - key0] = score; });
   __syncthreads();
 
   // ---- 2. keys in registers: thread tid holds positions 16*tid .. 16*tid+15
   uint32_t key[kRPer];
+  {
+    const float4* src = reinterpret_cast<const float4*>(sh.sc) + (kRPer / 4) * tid;
 #pragma unroll
-  for (int j = 0; j < kRPer; ++j) {
-    const int p = kRPer * tid + j;
-    key[j] = p < nr ? f2key(sh.sc[p]) : 0u;  // 0: past the range's keys
+    for (int q = 0; q < kRPer / 4; ++q) {
+      const float4 v = src[q];
+      const int p = kRPer * tid + 4 * q;
+      key[4 * q] = p < nr ? f2key(v.x) : 0u;  // 0: past the range's keys
+      key[4 * q + 1] = p + 1 < nr ? f2key(v.y) : 0u;
+      key[4 * q + 2] = p + 2 < nr ? f2key(v.z) : 0u;
+      key[4 * q + 3] = p + 3 < nr ? f2key(v.w) : 0u;
+    }
   }
   const int cnt = nr < K ? nr : K;
 
@@ -107,10 +124,15 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
     uint32_t lo = kmn;
     uint64_t range = kmx >= kmn ? (uint64_t)kmx - kmn + 1 : 1;
     need = (uint32_t)K;
+    bool ranked = false;
+    // Each pass narrows [lo, lo + range) to the bin holding the need-th
+    // largest remaining key.  Once that bin holds at most kRList keys, they
+    // are ranked directly under (key desc, position asc) instead.
     while (range > 1) {
       const int shift = bin_shift(range);
       const int nb = (int)((range - 1) >> shift) + 1;
       for (int i = tid; i < kRBins; i += kRNT) sh.hist[i] = 0;
+      if (tid == 0) sh.list_n = 0;
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kRPer; ++j) {
@@ -134,11 +156,12 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
         if (above < need && need <= above + cb[q]) {
           sh.found_bin = (uint32_t)(hb - q);
           sh.found_above = above;
+          sh.found_cnt = cb[q];
         }
         above += cb[q];
       }
       __syncthreads();
-      const uint32_t bsel = sh.found_bin, above_sel = sh.found_above;
+      const uint32_t bsel = sh.found_bin, above_sel = sh.found_above, in_bin = sh.found_cnt;
       __syncthreads();
       need -= above_sel;
       const uint64_t off = (uint64_t)bsel << shift;
@@ -146,11 +169,47 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
       const uint64_t rest = range - off;
       const uint64_t width = (uint64_t)1 << shift;
       range = rest < width ? rest : width;
+      if (range > 1 && in_bin <= (uint32_t)kRList) {
+        // the in_bin keys of [lo, lo + range): the need-th of them under
+        // (key desc, position asc) is the last one kept
+#pragma unroll
+        for (int j = 0; j < kRPer; ++j) {
+          const uint32_t k = key[j];
+          if (k && k >= lo && (uint64_t)(k - lo) < range) {
+            const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+            sh.lkey[slot] = k;
+            sh.lpos[slot] = kRPer * tid + j;
+          }
+        }
+        __syncthreads();
+        if (tid < (int)in_bin) {
+          const uint32_t mk = sh.lkey[tid];
+          const int mp = sh.lpos[tid];
+          const uint64_t mine = composite(mk, mp);
+          uint32_t rank = 0, eq_upto = 0;
+          for (int i = 0; i < (int)in_bin; ++i) {
+            const uint32_t k = sh.lkey[i];
+            const int p = sh.lpos[i];
+            rank += composite(k, p) < mine;
+            eq_upto += k == mk && p <= mp;
+          }
+          if (rank == need - 1) {
+            sh.found_key = mk;
+            sh.found_need = eq_upto;
+          }
+        }
+        __syncthreads();
+        T = sh.found_key;
+        need = sh.found_need;
+        ranked = true;
+        break;
+      }
     }
-    T = lo;
+    if (!ranked) T = lo;
   }
 
-  // ---- 3. ordered pass: keys > T, then the first `need` keys == T
+  // ---- 3. ordered pass: keys > T, then the first `need` keys == T, staged in
+  // LDS in position order and written out coalesced
   uint32_t cgt = 0, ceq = 0;
 #pragma unroll
   for (int j = 0; j < kRPer; ++j) {
@@ -160,8 +219,8 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
   uint32_t tot;
   const uint32_t pre = block_excl<kRNW>(cgt | (ceq << 16), sh.scan[pp], tot);
   uint32_t g = pre & 0xffffu, e = pre >> 16;
-  float* crow = cscore + (int64_t)t * ldc + (int64_t)r * K;
-  int32_t* prow = cpos + (int64_t)t * ldc + (int64_t)r * K;
+  float* stage_val = sh.sc;                                          // [K]
+  int32_t* stage_pos = reinterpret_cast<int32_t*>(sh.sc + kMaxTopK);  // [K]
 #pragma unroll
   for (int j = 0; j < kRPer; ++j) {
     const uint32_t k = key[j];
@@ -170,12 +229,19 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
     if (gt || (eq && e < need)) {
       const uint32_t slot = g + (e < need ? e : need);
       if ((int)slot < cnt) {
-        crow[slot] = key2f(k);
-        prow[slot] = key0 + kRPer * tid + j;
+        stage_val[slot] = key2f(k);
+        stage_pos[slot] = key0 + kRPer * tid + j;
       }
     }
     g += gt;
     e += eq;
+  }
+  __syncthreads();
+  float* crow = cscore + (int64_t)t * ldc + (int64_t)r * K;
+  int32_t* prow = cpos + (int64_t)t * ldc + (int64_t)r * K;
+  for (int i = tid; i < cnt; i += kRNT) {
+    crow[i] = stage_val[i];
+    prow[i] = stage_pos[i];
   }
 }
 

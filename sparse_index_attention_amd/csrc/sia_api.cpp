@@ -82,11 +82,11 @@ static int check_kv(const sia_kv_in* kv, sia_dtype q_dtype, int heads, int K) {
   if (kv->latent_dim < 1 || kv->rope_dim < 0) return SIA_ERR_INVALID_ARG;
   if (kv->dtype == SIA_F32) {
     if (q_dtype != SIA_F32) return SIA_ERR_UNSUPPORTED;
-    if (heads < 1 || heads > 64 || kv->latent_dim + kv->rope_dim > 1024 || K > 2048) return SIA_ERR_UNSUPPORTED;
+    if (heads < 1 || heads > 64 || kv->latent_dim + kv->rope_dim > 1024 || K > kMaxTopK) return SIA_ERR_UNSUPPORTED;
     return SIA_OK;
   }
   if (kv->dtype != SIA_BF16 && kv->dtype != SIA_FP8_E4M3) return SIA_ERR_UNSUPPORTED;
-  if (K > 2048) return SIA_ERR_UNSUPPORTED;
+  if (K > kMaxTopK) return SIA_ERR_UNSUPPORTED;
   if (q_dtype != SIA_BF16) return SIA_ERR_UNSUPPORTED;
   if (kv->latent_dim != 512 || kv->rope_dim != 64) return SIA_ERR_UNSUPPORTED;
   if (heads != 32 && heads != 64 && heads != 128) return SIA_ERR_UNSUPPORTED;
@@ -152,7 +152,7 @@ static size_t index_topk_ws_bytes(const sia_seqmap& seq, int K) {
 static int check_select(int K, int order) {
   if (K < 1 || order < SIA_ORDER_SCORE || order > SIA_SELECT_PAGES) return SIA_ERR_INVALID_ARG;
   if (order == SIA_SELECT_PAGES && K % 64 != 0) return SIA_ERR_INVALID_ARG;
-  if (K > 2048) return SIA_ERR_UNSUPPORTED;
+  if (K > kMaxTopK) return SIA_ERR_UNSUPPORTED;
   return SIA_OK;
 }
 
@@ -227,7 +227,7 @@ int sia_topk(const float* scores, int64_t ld, const sia_seqmap* seq, int32_t K, 
   if (rc) return rc;
   rc = check_scores(scores, ld, seq);
   if (rc) return rc;
-  if (K < 1 || K > 2048 || (order != 0 && order != 1)) return K > 2048 ? SIA_ERR_UNSUPPORTED : SIA_ERR_INVALID_ARG;
+  if (K < 1 || K > kMaxTopK || (order != 0 && order != 1)) return K > kMaxTopK ? SIA_ERR_UNSUPPORTED : SIA_ERR_INVALID_ARG;
   if (seq->num_tokens == 0) return SIA_OK;
   if (!idx) return SIA_ERR_INVALID_ARG;
   const hipError_t e = launch_topk(scores, ld, seq_args(*seq), K, order, idx, vals, stream);

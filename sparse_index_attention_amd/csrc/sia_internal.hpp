@@ -54,6 +54,7 @@ hipError_t launch_quantize_q(const void* q_bf16, int T, int heads, int dim, bool
                              hipStream_t st);
 // index_topk.hip
 constexpr int kIndexTopkRangeKeys = 8192;
+constexpr int kMaxTopK = 2048;  // largest K any entry point accepts
 int index_topk_ranges(int max_visible);
 // leading dimension of the candidate lists (a multiple of 4 floats)
 int64_t index_topk_ld(int max_visible, int K);
