@@ -459,8 +459,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     }
   };
   v16f sacc;   // full S^T of the tile the next iteration finishes
-  // gather of tile i+2 spread over the score steps: source rows first, then
-  // one 16-byte request per lane and step
+  // gather of tile i+2: source rows first, then every 16-byte request right
+  // after the first score MFMA (issued together, they land earlier than when
+  // spread over the score steps)
   auto dma_src = [&](int i, int k) __attribute__((always_inline)) -> const unsigned char* {
     const int r = 8 * (wave + NW * k) + (lane >> 3);
     const int slot = sslot[i * kRowsTile + r];
@@ -484,7 +485,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     float tloc = -INFINITY, psum = 0.f, mneg = 0.f;
     v8bf pb[2];
     auto soft = [&](int j) __attribute__((always_inline)) {
-      if (j < kRG * 9) dma_one(dsrc[j / 9], fut, j / 9, j % 9);
+      if (j == 0) {
+#pragma unroll
+        for (int d = 0; d < kRG * 9; ++d) dma_one(dsrc[d / 9], fut, d / 9, d % 9);
+      }
       if (j == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
