@@ -126,6 +126,9 @@ __global__ __launch_bounds__(256) void k_sparse_mla_f32(MlaArgs a) {
 constexpr int kDc = 512, kDr = 64, kD = kDc + kDr;
 constexpr int kChunks = kD / 8;                   // 72 chunks of 8 bf16 (16 bytes) per row
 constexpr int kRowsTile = 32;
+constexpr int kRawBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
+// read for latent rows without a valid index when the pool is addressed directly
+__device__ uint4 g_zero_kv_row[kD * 2 / 16];
 constexpr int kTileBytes = kRowsTile * kD * 2;   // 36864
 
 // Chunk swizzle of a tile row: bit 1 of the row -> bit 2, bit 3 -> bit 1, bit 2
@@ -181,7 +184,7 @@ constexpr int kVT = kVH / 32;  // 32-column output tiles per half
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
 template <int N> __device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N)); }
 
-template <int NW, bool FP8>
+template <int NW, bool FP8, bool BUF>
 __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   constexpr int NT = NW * 64;
   constexpr int HBW = NW / 2;                  // head blocks per workgroup
@@ -226,54 +229,45 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   // wave instruction (row group rg, chunk group m) covers rows 8rg..8rg+7 and
   // chunks 8m..8m+7; lane L: row 8rg + L/8, chunk 8m + ((L%8) ^ swz(row)), so
   // that one 16-byte LDS write per lane fills 64 consecutive slots (1 KB).
-  // The rows pass through registers: the next tile is loaded while this one is
-  // computed and written to LDS after it.  (Direct global->LDS loads would keep
-  // a load that may touch LDS in flight during the whole tile, and the compiler
-  // then waits for every outstanding LDS read at each operand use.)
   const int g_sub = lane & 7;
   constexpr int kRG = (4 + NW - 1) / NW;   // 8-row groups per wave
-  v4i bstage[FP8 ? 1 : kRG * 9];
-  auto issue_bf16 = [&](int i) __attribute__((always_inline)) {
-    const int32_t* ss = sslot + i * kRowsTile;
-#pragma unroll
-    for (int k = 0; k < kRG; ++k) {
-      const int r = 8 * (wave + NW * k) + (lane >> 3);
-      const int slot = ss[r] >= 0 ? ss[r] : 0;
-      const unsigned char* src = kvb + (int64_t)slot * (kD * 2) + 16 * (g_sub ^ swz(r));
-#pragma unroll
-      for (int m = 0; m < 9; ++m) bstage[k * 9 + m] = *(const v4i*)(src + 128 * m);
-    }
-  };
-  // the same loads one at a time (q = 9k + m), for interleaving with MFMAs
-  auto bf16_src = [&](int i, int k) __attribute__((always_inline)) -> const unsigned char* {
-    const int r = 8 * (wave + NW * k) + (lane >> 3);
-    const int slot = sslot[i * kRowsTile + r];
-    return kvb + (int64_t)(slot >= 0 ? slot : 0) * (kD * 2) + 16 * (g_sub ^ swz(r));
-  };
-  auto commit_bf16_one = [&](lds_u8* dst, int q) __attribute__((always_inline)) {
-    *(lds_v4i*)(dst + 4096 * (q % 9) + 1024 * (wave + NW * (q / 9)) + 16 * lane) = bstage[q];
-  };
-  auto commit_bf16 = [&](lds_u8* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = 0; k < kRG; ++k)
-#pragma unroll
-      for (int m = 0; m < 9; ++m)
-        *(lds_v4i*)(dst + 4096 * m + 1024 * (wave + NW * k) + 16 * lane) = bstage[k * 9 + m];
-  };
 
-  // the same rows straight into LDS (bf16 pipeline below): one wave instruction
-  // fills the 64 consecutive 16-byte slots of (row group, chunk group)
+  // A pool below 4 GiB is addressed through a buffer descriptor (BUF): with a
+  // global request in flight the compiler waits for every outstanding LDS read
+  // before using any one of them, with a buffer request only for the one it
+  // needs, so the operand prefetch keeps working while the gather flies.
+  // Rows without a valid index are loaded as zeros (an offset past the
+  // descriptor's range, or a zero row), so that whatever the pool holds in
+  // the row they would otherwise read, they contribute exactly nothing.
+  const uint32_t kv_bytes = (uint32_t)((uint64_t)a.s.num_pages * kPage * (kD * 2));  // BUF only
+  const __amdgpu_buffer_rsrc_t kvrs = __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)kv_bytes, kRawBufferWord3);
+  // source of lane's 16-byte piece of chunk group 0 of tile row r: a buffer
+  // offset (BUF) or an address
+  auto row_src = [&](int slot, int r) __attribute__((always_inline)) -> uint64_t {
+    const uint32_t piece = 16 * (g_sub ^ swz(r));
+    if constexpr (BUF)
+      return slot >= 0 ? (uint64_t)slot * (kD * 2) + piece : (uint64_t)kv_bytes + piece;
+    else
+      return slot >= 0 ? (uint64_t)(uintptr_t)(kvb + (uint64_t)slot * (kD * 2) + piece)
+                       : (uint64_t)(uintptr_t)((const unsigned char*)g_zero_kv_row + piece);
+  };
+  auto row_req = [&](uint64_t src, lds_u8* dst) __attribute__((always_inline)) {
+    if constexpr (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kvrs, (lds_void*)dst, 16, (uint32_t)src, 0, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(uintptr_t)src,
+                                       (lds_void*)dst, 16, 0, 0);
+  };
+  // one wave instruction fills the 64 consecutive 16-byte slots of (row group,
+  // chunk group)
   auto issue_dma = [&](int i, lds_u8* dst) __attribute__((always_inline)) {
     const int32_t* ss = sslot + i * kRowsTile;
 #pragma unroll
     for (int k = 0; k < kRG; ++k) {
       const int r = 8 * (wave + NW * k) + (lane >> 3);
-      const int slot = ss[r] >= 0 ? ss[r] : 0;
-      const unsigned char* src = kvb + (int64_t)slot * (kD * 2) + 16 * (g_sub ^ swz(r));
+      const uint64_t src = row_src(ss[r], r);
 #pragma unroll
-      for (int m = 0; m < 9; ++m)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 128 * m),
-                                         (lds_void*)(dst + 4096 * m + 1024 * (wave + NW * k)), 16, 0, 0);
+      for (int m = 0; m < 9; ++m) row_req(src + 128 * m, dst + 4096 * m + 1024 * (wave + NW * k));
     }
   };
 
@@ -284,7 +278,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   const int f_row = tid / TPR, f_sub = tid % TPR;
   auto issue_fp8 = [&](int i) __attribute__((always_inline)) {
     const int32_t* ss = sslot + i * kRowsTile;
-    const int slot = ss[f_row] >= 0 ? ss[f_row] : 0;
+    const bool valid = ss[f_row] >= 0;  // otherwise zeros, whatever slot 0 holds
+    const int slot = valid ? ss[f_row] : 0;
     const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
     const int page = slot >> 6, tok = slot & 63;
     const int tiles_tok = kPage / a.scale_tokens, tiles_el = kDc / a.scale_elems;
@@ -292,8 +287,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
 #pragma unroll
     for (int m = 0; m < kFp8Loads; ++m) {
       const int c = f_sub + TPR * m;
-      stage[m] = *(const v4i*)(src + 16 * TPR * m);
-      stage_scale[m] = c < 32 ? a.kv_scale[sbase + (16 * c) / a.scale_elems] : 1.f;
+      const v4i v = *(const v4i*)(src + 16 * TPR * m);
+      stage[m] = valid ? v : v4i{0, 0, 0, 0};
+      const float sc = c < 32 ? a.kv_scale[sbase + (16 * c) / a.scale_elems] : 1.f;
+      stage_scale[m] = valid ? sc : 0.f;
     }
   };
   auto commit_fp8 = [&](lds_u8* dst) __attribute__((always_inline)) {
@@ -462,17 +459,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   // gather of tile i+2: source rows first, then every 16-byte request right
   // after the first score MFMA (issued together, they land earlier than when
   // spread over the score steps)
-  auto dma_src = [&](int i, int k) __attribute__((always_inline)) -> const unsigned char* {
+  auto dma_src = [&](int i, int k) __attribute__((always_inline)) -> uint64_t {
     const int r = 8 * (wave + NW * k) + (lane >> 3);
-    const int slot = sslot[i * kRowsTile + r];
-    return kvb + (int64_t)(slot >= 0 ? slot : 0) * (kD * 2) + 16 * (g_sub ^ swz(r));
+    return row_src(sslot[i * kRowsTile + r], r);
   };
-  auto dma_one = [&](const unsigned char* src, lds_u8* dst, int k, int m) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 128 * m),
-                                     (lds_void*)(dst + 4096 * m + 1024 * (wave + NW * k)), 16, 0, 0);
+  auto dma_one = [&](uint64_t src, lds_u8* dst, int k, int m) __attribute__((always_inline)) {
+    row_req(src + 128 * m, dst + 4096 * m + 1024 * (wave + NW * k));
   };
   auto iter = [&](int i, lds_u8* cur, lds_u8* nxt, lds_u8* fut) __attribute__((always_inline)) {
-    const unsigned char* dsrc[kRG];
+    uint64_t dsrc[kRG];
 #pragma unroll
     for (int k = 0; k < kRG; ++k) dsrc[k] = dma_src(i + 2, k);
     const Flags fl = load_flags(i);
@@ -582,13 +577,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   if (pass == 1) m_ref = m_seen;
   // prologue: tile 0 staged and written
   if (ntiles > 0) {
-    if constexpr (FP8) {
-      issue_fp8(0);
-      commit_fp8(T0);
-    } else {
-      issue_bf16(0);
-      commit_bf16(T0);
-    }
+    issue_fp8(0);
+    commit_fp8(T0);
   }
 
   // one tile: compute on `cur` while tile i+1 is loaded into registers, then
@@ -597,17 +587,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     // every wave's LDS writes of tile i are done (lgkmcnt 0) before the barrier;
     // the loads of tile i+1 are issued after it
     const bool has_next = i + 1 < ntiles;
-    // bf16: source rows of tile i+1 (slot table reads, before the barrier)
-    const unsigned char* nsrc[FP8 ? 1 : kRG];
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int k = 0; k < kRG; ++k) nsrc[k] = bf16_src(has_next ? i + 1 : i, k);
-    }
     wait_vm_lgkm0<63>();
     asm volatile("s_barrier" ::: "memory");
-    if constexpr (FP8) {
-      if (has_next) issue_fp8(i + 1);
-    }
+    if (has_next) issue_fp8(i + 1);
     const int32_t* ss = sslot + i * kRowsTile;
 
     // validity of this lane's 16 rows: rows 8k + 4hh + 0..3 are four consecutive slots
@@ -627,10 +609,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const v8bf kf = kring[j % PF];
       if (j + PF < kHalfSteps) kring[j % PF] = *(lds_v8bf*)(cur + sbase[(j + PF) & 1] + 4096 * ((j + PF) >> 1));
       sacc = mfma_bf16(kf, qb[j], sacc);
-      // one row load of tile i+1 per step, in the shadow of the MFMAs
-      if constexpr (!FP8) {
-        if (j < kRG * 9 && has_next) bstage[j] = *(const v4i*)(nsrc[j / 9] + 128 * (j % 9));
-      }
       // keep each prefetch PF steps ahead of its use (the scheduler would sink it)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -696,21 +674,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       if (k + PF < 2 * kVT) vring[k % PF] = vfrag((k + PF) % kVT, (k + PF) / kVT);
       o[vt] = mfma_bf16(af, pb[mf], o[vt]);
       if (k < 8) pexp(8 + k);
-      if constexpr (!FP8) {
-        if (k < kRG * 9 && has_next) commit_bf16_one(nxt1, k);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += psum;
 
-    if (has_next) {
-      if constexpr (FP8) {
-        commit_fp8(nxt1);
-      } else {
-#pragma unroll
-        for (int q = 2 * kVT; q < kRG * 9; ++q) commit_bf16_one(nxt1, q);
-      }
-    }
+    if (has_next) commit_fp8(nxt1);
   };
   // Whole triples in the loop and the remainder after it: a loop body with
   // conditionally skipped steps merges differently ordered in-flight loads at
@@ -878,11 +846,16 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nblocks);
   const bool fp8 = kv.dtype == SIA_FP8_E4M3;
+  // bf16 pools that buffer offsets (32 bits) can address take the buffer form
+  // (with room past the end for the zero-row offsets)
+  const bool buf = (uint64_t)s.num_pages * kPage * (kD * 2) <= 0xfffff000ull;
 #define SIA_LAUNCH_MLA(NW)                                                                   \
   if (fp8)                                                                                   \
-    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true>), grid, dim3(NW * 64), 0, st, a);        \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, false>), grid, dim3(NW * 64), 0, st, a); \
+  else if (buf)                                                                              \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false, true>), grid, dim3(NW * 64), 0, st, a); \
   else                                                                                       \
-    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false, false>), grid, dim3(NW * 64), 0, st, a);
   if (heads >= 64) {
     SIA_LAUNCH_MLA(4)
   } else {

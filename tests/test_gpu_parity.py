@@ -242,6 +242,74 @@ def test_permuted_block_table_matches_identity():
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
 
 
+def test_sparse_mla_pool_beyond_4gib():
+    """A bf16 latent pool under 4 GiB is gathered through 32-bit buffer offsets,
+    a larger one through 64-bit addresses.  The same pages placed at the top of
+    a 4.4 GB pool (offsets past 2^32, every other page NaN) give bit-identical
+    outputs, and both match the oracle."""
+    wl = workload("decode_tiny")
+    K, H = wl.cfg["K"], wl.cfg["H"]
+    seq, _, q, kv = upload(wl)
+    _, sel, att = oracle_run("decode_tiny")
+    idx = dev(np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32))
+    P = wl.kv.shape[0]
+    big_pages = 60000   # 60000 x 64 rows x 1152 bytes = 4.42 GB
+    assert big_pages * 64 * 1152 > 2**32 and P < big_pages
+    base = big_pages - P
+    print(f"[mla-big-pool] {P} pages placed at {base}..{big_pages - 1}", flush=True)
+    # every page the table does not name holds NaN: rows without a valid index
+    # must not read them
+    big = torch.full((big_pages,) + tuple(kv.pool.shape[1:]), float("nan"), dtype=kv.pool.dtype, device="cuda")
+    big[base:].copy_(kv.pool)
+    kv_big = sia.LatentKV(big, 512, 64)
+    seq_big = sia.SeqMap(seq.q_seq, seq.q_pos, seq.block_table + base, big_pages, wl.max_visible)
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        la = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+        lb = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+        a = fn(q, kv, seq, idx, K, wl.softmax_scale, lse=la)
+        b = fn(q, kv_big, seq_big, idx, K, wl.softmax_scale, lse=lb)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), fn.__name__
+        assert torch.equal(la, lb), fn.__name__
+        check_attention("bf16", to_np_out(b), lb.cpu().numpy(), att, range(wl.Tq))
+    del big
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["decode_tiny", "quant_decode_tiny", "prefill_tiny"])
+def test_sparse_mla_padding_rows_ignore_pool_contents(name):
+    """Index lists padded with -1 (and holes) must not depend on what the pool
+    holds in the row such entries would address: a NaN page placed at
+    physical page 0 (every real page moved up by one) leaves the outputs
+    bit-identical."""
+    wl = workload(name)
+    K, H = wl.cfg["K"], wl.cfg["H"]
+    seq, _, q, kv = upload(wl)
+    _, sel, _ = oracle_run(name)
+    ids = np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32)
+    ids[:, 1::7] = -1   # holes as well as trailing padding
+    idx = dev(ids)
+    print(f"[mla-nan-page0] {name}: {int((ids < 0).sum())} padded entries", flush=True)
+    if kv.pool.dtype == torch.uint8:   # fp8 codes 0xff and bf16 0xffff are NaN
+        pool2 = torch.cat([torch.full_like(kv.pool[:1], 0xFF), kv.pool])
+        scale2 = torch.cat([torch.full_like(kv.scale[:1], float("nan")), kv.scale])
+        kv2 = sia.LatentKV(pool2, kv.latent_dim, kv.rope_dim, scale2, kv.scale_tokens, kv.scale_elems)
+    else:
+        pool2 = torch.cat([torch.full_like(kv.pool[:1], float("nan")), kv.pool])
+        kv2 = sia.LatentKV(pool2, kv.latent_dim, kv.rope_dim)
+    seq2 = sia.SeqMap(seq.q_seq, seq.q_pos, seq.block_table + 1, seq.num_pages + 1, wl.max_visible)
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        la = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+        lb = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+        a = fn(q, kv, seq, idx, K, wl.softmax_scale, lse=la)
+        b = fn(q, kv2, seq2, idx, K, wl.softmax_scale, lse=lb)
+        torch.cuda.synchronize()
+        assert torch.isfinite(b.float()).all(), fn.__name__
+        assert torch.equal(a.view(torch.int16) if a.dtype != torch.float32 else a,
+                           b.view(torch.int16) if b.dtype != torch.float32 else b), fn.__name__
+        assert torch.equal(la, lb), fn.__name__
+
+
 def test_split_count_invariance():
     """Decode (rows split over workgroups, merged by LSE) equals prefill (one
     workgroup per token) within fp32 rounding of the merge."""
