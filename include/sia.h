@@ -244,7 +244,9 @@ int sia_quantize_indexer_q(const sia_indexer_in* in, int32_t num_tokens, void* q
  * all heads.  A token with no valid index gets out = 0 and lse = -inf.
  *   q     [T, heads, latent+rope]: SIA_BF16 for bf16/fp8 caches, SIA_F32 for f32
  *   out   [T, heads, latent] in q's dtype;  lse [T, heads] float or NULL
- *   idx   [T, K] int32 (-1 = unused slot)
+ *   idx   [T, K] int32 (-1 = unused slot; an unused slot, or a position
+ *         outside [0, max_visible), reads nothing from the pools and
+ *         contributes nothing, whatever the pool holds)
  * Supported: f32 cache with heads <= 64; bf16/fp8 cache with heads in
  * {32, 64, 128}.  1 <= K <= 2048.
  * _decode splits each token's rows over several workgroups and merges the
