@@ -197,7 +197,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char tile2[kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t sslot[kMaxSplitRows + 2 * kRowsTile];
-  __shared__ __attribute__((aligned(16))) float smask[FP8 ? 4 : kMaxSplitRows + 2 * kRowsTile];  // 0 or -inf per row
+  __shared__ __attribute__((aligned(16))) float smask[kMaxSplitRows + 2 * kRowsTile];  // 0 or -inf per row
   __shared__ __attribute__((aligned(16))) float4 xbuf[2 * NW * 4 * 64];   // partial S^T exchange, two parities
 
   // block -> (token, split, head part); blocks b and b + 8 share (token, split)
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const bool ok = r < rows && j0 + r < j1 && p >= 0 && p < a.s.max_visible;
       const int pg = clampi(page[u], 0, a.s.num_pages - 1);
       if (r < rows) sslot[r] = ok ? pg * kPage + (p & (kPage - 1)) : -1;
-      if (!FP8 && r < rows) smask[r] = ok ? 0.f : -INFINITY;
+      if (r < rows) smask[r] = ok ? 0.f : -INFINITY;
     }
   }
   // keep the query operand resident: without this the compiler re-loads it
@@ -397,15 +397,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   lds_u8* const T1 = (lds_u8*)tile1;
   lds_u8* const T2 = (lds_u8*)tile2;
   __syncthreads();
-  if constexpr (!FP8) {
-  // ---- bf16: software-pipelined tiles ------------------------------------
+  {
+  // ---- software-pipelined tiles ------------------------------------
   // Iteration i requests tile i+2 into the buffer tile i-1 used, computes the
   // partial scores of tile i+1 while the softmax of tile i runs between its
   // MFMAs, then O += V^T P^T for tile i, and ends with the one barrier that
-  // publishes tile i+2 and the partial scores of tile i+1.  Requests and score
-  // passes past the last tile run on the slot table's -1 padding (slot 0) and
-  // their results are never used; this keeps the loop free of conditional
-  // requests, which would make the compiler drain every load before each read.
+  // publishes tile i+2 and the partial scores of tile i+1.  bf16 rows go
+  // straight into LDS; fp8 rows are loaded into registers at the start of the
+  // iteration and dequantized into the buffer after the output MFMAs.
+  // Requests and score passes past the last tile run on the slot table's -1
+  // padding (zero rows) and their results are never used; this keeps the loop
+  // free of conditional requests, which would make the compiler drain every
+  // load before each read.
   // additive masks of this lane's 16 rows of tile i (rows 8k + 4hh + 0..3
   // are four consecutive entries)
   struct Flags {
@@ -468,8 +471,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   };
   auto iter = [&](int i, lds_u8* cur, lds_u8* nxt, lds_u8* fut) __attribute__((always_inline)) {
     uint64_t dsrc[kRG];
+    if constexpr (FP8) {
+      issue_fp8(i + 2);  // into registers; dequantized into LDS after the output MFMAs
+    } else {
 #pragma unroll
-    for (int k = 0; k < kRG; ++k) dsrc[k] = dma_src(i + 2, k);
+      for (int k = 0; k < kRG; ++k) dsrc[k] = dma_src(i + 2, k);
+    }
     const Flags fl = load_flags(i);
     // softmax of tile i (log2 domain; lane owns head nn, rows 8(r/4) + 4hh + r%4).
     // The maximum over both lane halves (one v_permlane32_swap) is needed only
@@ -480,9 +487,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     float tloc = -INFINITY, psum = 0.f, mneg = 0.f;
     v8bf pb[2];
     auto soft = [&](int j) __attribute__((always_inline)) {
-      if (j == 0) {
+      if constexpr (!FP8) {
+        if (j == 0) {
 #pragma unroll
-        for (int d = 0; d < kRG * 9; ++d) dma_one(dsrc[d / 9], fut, d / 9, d % 9);
+          for (int d = 0; d < kRG * 9; ++d) dma_one(dsrc[d / 9], fut, d / 9, d % 9);
+        }
       }
       if (j == 0) {
 #pragma unroll
@@ -531,6 +540,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       o[vt] = mfma_bf16(af, pb[mf], o[vt]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (FP8) commit_fp8(fut);  // tile i+2: buffer free since the last barrier
     l_run += psum;
     // tile i+2 is in LDS and the partial scores of tile i+1 are published
     wait_vm_lgkm0<0>();
@@ -548,8 +558,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       m_ref = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     // prologue: tiles 0 and 1 in LDS, full scores of tile 0
-    issue_dma(0, T0);
-    issue_dma(1, T1);
+    if constexpr (FP8) {
+      issue_fp8(0);
+      commit_fp8(T0);
+      issue_fp8(1);
+      commit_fp8(T1);
+    } else {
+      issue_dma(0, T0);
+      issue_dma(1, T1);
+    }
     wait_vm_lgkm0<0>();
     asm volatile("s_barrier" ::: "memory");
     sacc = s_partial(T0, [](int) {});
@@ -567,132 +584,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     if (i + 1 < ntiles) iter(i + 1, T1, T2, T0);
     // every wave agrees on a second pass; the barrier also retires this pass's tiles
     if (!__syncthreads_or(overflow)) break;
-  }
-  } else {
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-  for (int v = 0; v < kVT; ++v) o[v] = v16f{};
-  l_run = 0.f;
-  overflow = false;
-  if (pass == 1) m_ref = m_seen;
-  // prologue: tile 0 staged and written
-  if (ntiles > 0) {
-    issue_fp8(0);
-    commit_fp8(T0);
-  }
-
-  // one tile: compute on `cur` while tile i+1 is loaded into registers, then
-  // write it into `nxt1` (last read two tiles ago, before this tile's barrier)
-  auto tile_step = [&](int i, lds_u8* cur, lds_u8* nxt1, lds_u8* nxt2) __attribute__((always_inline)) {
-    // every wave's LDS writes of tile i are done (lgkmcnt 0) before the barrier;
-    // the loads of tile i+1 are issued after it
-    const bool has_next = i + 1 < ntiles;
-    wait_vm_lgkm0<63>();
-    asm volatile("s_barrier" ::: "memory");
-    if (has_next) issue_fp8(i + 1);
-    const int32_t* ss = sslot + i * kRowsTile;
-
-    // validity of this lane's 16 rows: rows 8k + 4hh + 0..3 are four consecutive slots
-    int4 vflag[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) vflag[k] = *(const int4*)(ss + 8 * k + 4 * hh);
-
-    // partial S^T = KV . Q^T over this wave's half of the depth (rows x heads),
-    // operands loaded PF steps ahead
-    constexpr int PF = 3;
-    v16f sacc = v16f{};
-    v8bf kring[PF];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) kring[j] = *(lds_v8bf*)(cur + sbase[j & 1] + 4096 * (j >> 1));
-#pragma unroll
-    for (int j = 0; j < kHalfSteps; ++j) {
-      const v8bf kf = kring[j % PF];
-      if (j + PF < kHalfSteps) kring[j % PF] = *(lds_v8bf*)(cur + sbase[(j + PF) & 1] + 4096 * ((j + PF) >> 1));
-      sacc = mfma_bf16(kf, qb[j], sacc);
-      // keep each prefetch PF steps ahead of its use (the scheduler would sink it)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // exchange the partial sums with the other wave of the head block; both
-    // waves add the same two fp32 values, so both hold the same S^T
-    {
-      float4* mine = xbuf + wave * 256 + lane;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) mine[64 * k] = make_float4(sacc[4 * k], sacc[4 * k + 1], sacc[4 * k + 2], sacc[4 * k + 3]);
-      wait_vm_lgkm0<63>();
-      asm volatile("s_barrier" ::: "memory");
-      const float4* other = xbuf + partner * 256 + lane;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v = other[64 * k];
-        sacc[4 * k] += v.x;
-        sacc[4 * k + 1] += v.y;
-        sacc[4 * k + 2] += v.z;
-        sacc[4 * k + 3] += v.w;
-      }
-    }
-    // online softmax over the tile's rows (log2 domain); lane owns head nn,
-    // rows 8*(r/4) + 4*hh + r%4
-    float sv[16];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int4 f = vflag[r >> 2];
-      const int slot = (r & 3) == 0 ? f.x : (r & 3) == 1 ? f.y : (r & 3) == 2 ? f.z : f.w;
-      sv[r] = slot >= 0 ? sacc[r] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    m_seen = fmaxf(m_seen, tmax);
-    if (m_ref == -INFINITY) m_ref = tmax;
-    overflow |= tmax > m_ref + 100.f;
-    float psum = 0.f;
-    v8bf pb[2];
-    auto pexp = [&](int r) __attribute__((always_inline)) {
-      const float pv = (m_ref == -INFINITY) ? 0.f : fast_exp2(sv[r] - m_ref);
-      psum += pv;
-      pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
-    };
-#pragma unroll
-    for (int r = 0; r < 8; ++r) pexp(r);
-
-    // O^T += V^T . P^T ; MFMA mf covers tile rows 16mf + R(hh, jj); operands one step ahead
-    auto vfrag = [&](int vt, int mf) -> v8bf {
-      const int imm = 4096 * (vt >> 1) + 2048 * mf;
-      const v4bf x0 = lds_tr16(cur, vbase[vt & 1][0] + imm);
-      const v4bf x1 = lds_tr16(cur, vbase[vt & 1][1] + imm);
-      return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    // step k: column tile k % kVT, row half k / kVT (P rows 8..15 are computed
-    // during the first half); one LDS write of tile i+1 per step
-    v8bf vring[PF];
-#pragma unroll
-    for (int k = 0; k < PF; ++k) vring[k] = vfrag(k % kVT, k / kVT);
-#pragma unroll
-    for (int k = 0; k < 2 * kVT; ++k) {
-      const int vt = k % kVT, mf = k / kVT;
-      const v8bf af = vring[k % PF];
-      if (k + PF < 2 * kVT) vring[k % PF] = vfrag((k + PF) % kVT, (k + PF) / kVT);
-      o[vt] = mfma_bf16(af, pb[mf], o[vt]);
-      if (k < 8) pexp(8 + k);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    l_run += psum;
-
-    if (has_next) commit_fp8(nxt1);
-  };
-  // Whole triples in the loop and the remainder after it: a loop body with
-  // conditionally skipped steps merges differently ordered in-flight loads at
-  // its head, and the compiler then drains every load before reading a tile.
-  int i = 0;
-  for (; i + 3 <= ntiles; i += 3) {
-    tile_step(i, T0, T1, T2);
-    tile_step(i + 1, T1, T2, T0);
-    tile_step(i + 2, T2, T0, T1);
-  }
-  if (i < ntiles) tile_step(i, T0, T1, T2);
-  if (i + 1 < ntiles) tile_step(i + 1, T1, T2, T0);
-  // every wave agrees on a second pass; the barrier also retires this pass's tiles
-  if (!__syncthreads_or(overflow)) break;
   }
   }
 
