@@ -437,7 +437,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       if (j + PF < kHalfSteps) kring[j % PF] = *(lds_v8bf*)(buf + sbase[(j + PF) & 1] + 4096 * ((j + PF) >> 1));
       acc = mfma_bf16(kf, qb[j], acc);
       between(j);
-      
     }
     return acc;
   };
@@ -538,7 +537,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const v8bf af = vring[k % PFV];
       if (k + PFV < 2 * kVT) vring[k % PFV] = vfrag((k + PFV) % kVT, (k + PFV) / kVT);
       o[vt] = mfma_bf16(af, pb[mf], o[vt]);
-      
     }
     if constexpr (FP8) commit_fp8(fut);  // tile i+2: buffer free since the last barrier
     l_run += psum;
