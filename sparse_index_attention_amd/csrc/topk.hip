@@ -293,18 +293,37 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   // ---- 1. keys, range, sample ----------------------------------------------------
   uint32_t key[PER > 0 ? PER : 1];
   if constexpr (PER > 0) {
+    if constexpr (PER <= 32) {
+      // every load is unconditional, so that they are all in flight together
+      // instead of one branch, and one memory latency, at a time; a group past
+      // the visible keys re-reads the row's first four floats (a cache hit)
+      // rather than fetching keys it would mask.  Masks rather than selects: a
+      // select lets the compiler move a load under a branch and wait there.
 #pragma unroll
-    for (int j = 0; j < PER / 4; ++j) {
-      const int i = (j * kNT + tid) * 4;
-      if (i + 4 <= n) {
-        const float4 v = *reinterpret_cast<const float4*>(row + i);
-        key[4 * j] = f2key(v.x);
-        key[4 * j + 1] = f2key(v.y);
-        key[4 * j + 2] = f2key(v.z);
-        key[4 * j + 3] = f2key(v.w);
-      } else {
+      for (int j = 0; j < PER / 4; ++j) {
+        const int i = (j * kNT + tid) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(row + (i < n && i + 4 <= ld ? i : 0));
+        key[4 * j] = f2key(v.x) & (0u - (uint32_t)(i < n));
+        key[4 * j + 1] = f2key(v.y) & (0u - (uint32_t)(i + 1 < n));
+        key[4 * j + 2] = f2key(v.z) & (0u - (uint32_t)(i + 2 < n));
+        key[4 * j + 3] = f2key(v.w) & (0u - (uint32_t)(i + 3 < n));
+      }
+    } else {
+      // 64 keys per thread: loading them all at once would not fit the
+      // registers of 16 waves, so the loads stay per group
 #pragma unroll
-        for (int q = 0; q < 4; ++q) key[4 * j + q] = i + q < n ? f2key(row[i + q]) : 0u;
+      for (int j = 0; j < PER / 4; ++j) {
+        const int i = (j * kNT + tid) * 4;
+        if (i + 4 <= n) {
+          const float4 v = *reinterpret_cast<const float4*>(row + i);
+          key[4 * j] = f2key(v.x);
+          key[4 * j + 1] = f2key(v.y);
+          key[4 * j + 2] = f2key(v.z);
+          key[4 * j + 3] = f2key(v.w);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) key[4 * j + q] = i + q < n ? f2key(row[i + q]) : 0u;
+        }
       }
     }
   } else {
