@@ -27,6 +27,8 @@ METRIC = "query tokens/s for index+TopK+sparse-MLA; decode µs/step; % HBM/MFMA 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
+# published fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed fp32) x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -35,7 +37,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "quant_decode", "long_prefill", "cp_chunk_prefill", "tiny_prefill", "mx_decode", "bf16_decode"])
+                   choices=["decode", "quant_decode", "quant_decode_tile128", "long_prefill", "cp_chunk_prefill",
+                            "tiny_prefill", "mx_decode", "bf16_decode"])
     p.add_argument("--copies", type=int, default=3, help="distinct device copies of the inputs (decode)")
     p.add_argument("--order", type=int, default=0, choices=[0, 1, 2],
                    help="selection: Top-K positions score-sorted (0) or by position (1), or whole pages (2)")
@@ -60,6 +63,9 @@ TRAFFIC_KERNELS = {                 # roofline kernel -> (kernel-name substrings
                    ("sparse_mla.hip", "sia_common.hpp", "sia_internal.hpp")),
     "index_scores": (("k_index_scores_fp8",),
                      ("indexer.hip", "index_core.hpp", "block_prims.hpp", "sia_common.hpp", "sia_internal.hpp")),
+    "index_topk": (("k_index_topk_ranges", "k_topk"),
+                   ("index_topk.hip", "topk.hip", "index_core.hpp", "block_prims.hpp", "sia_common.hpp",
+                    "sia_internal.hpp")),
 }
 
 
@@ -149,8 +155,9 @@ def algorithmic_work(wl):
         q_b = Hi * Di * (1 if c["idx_dtype"] == "fp8" else 4) + 4 * Hi + 4
     if c["kv_dtype"] == "bf16":
         row_b = 2 * (Dc + Dr)
-    elif c["kv_dtype"] == "fp8":
-        row_b = Dc + 2 * Dr + 4 * (1 if c["kv_scale"] == (1, 128) else 0)
+    elif c["kv_dtype"] == "fp8":     # codes, bf16 rope, and the row's share of its tile scales
+        st, se = c["kv_scale"]
+        row_b = Dc + 2 * Dr + 4.0 * (Dc // se) / st
     else:
         row_b = 4 * (Dc + Dr)
     elt = 4 if c["kv_dtype"] == "f32" else 2
@@ -158,31 +165,57 @@ def algorithmic_work(wl):
     idx_flops = float(vis.sum() * 2 * Hi * Di)
     mla_bytes = float(sel.sum() * (row_b + 4) + wl.Tq * H * ((Dc + Dr) + Dc) * elt)
     mla_flops = float(sel.sum() * 2 * H * ((Dc + Dr) + Dc))
-    return {"index_scores": (idx_bytes, idx_flops), "topk": (float(wl.Tq * K * 4), 0.0),
-            "sparse_mla": (mla_bytes, mla_flops)}
+    topk_bytes = float(wl.Tq * K * 4)
+    return {"index_scores": (idx_bytes, idx_flops), "topk": (topk_bytes, 0.0),
+            "index_topk": (idx_bytes + topk_bytes, idx_flops), "sparse_mla": (mla_bytes, mla_flops)}
+
+
+def roofline_peak(wl, kernel):
+    """(bound, peak, unit) of an entry point on this workload: decode steps are
+    HBM-bound; prefill indexers run on the MFMA of their operand type, sparse
+    MLA on the bf16 MFMA (fp8 latent rows are dequantized to bf16); the fp32
+    path runs on the vector ALU."""
+    c = wl.cfg
+    if c["kind"] == "decode":
+        return "hbm", HBM_PEAK_GBS, "GB/s"
+    dt = c["idx_dtype"] if kernel in ("index_scores", "index_topk") else c["kv_dtype"]
+    if dt == "f32":
+        return "alu", FP32_VALU_PEAK_TFLOPS, "TFLOP/s"
+    if kernel in ("index_scores", "index_topk") and dt in ("fp8", "mxfp8"):
+        return "mfma", FP8_PEAK_TFLOPS, "TFLOP/s"
+    return "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
 
 
 def cpu_baseline(wl, budget_s):
     """The oracle as it stands, on a bounded sample of the same workload."""
+    import contextlib
+
     import numpy as np
     import oracle as O
+    # the host cores this process may run on, capped by the thread limit the
+    # environment sets for math libraries; BLAS is limited to that many threads
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        cores = min(cores, int(omp))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores)
     except Exception:
-        cores = 1
+        limit = contextlib.nullcontext()
     K = wl.cfg["K"]
     rows = list(np.argsort(-wl.q_pos, kind="stable")) if wl.cfg["kind"] != "decode" else list(range(wl.Tq))
     rng = np.random.default_rng(0)
     if wl.cfg["kind"] != "decode":
         rows = list(rng.choice(wl.Tq, size=min(wl.Tq, 64), replace=False))
     done, t0 = [], time.perf_counter()
-    for t in rows:
-        O.index_select_attend(wl.oracle_indexer(), wl.q, wl.oracle_kv(), wl.oracle_seq(), K, wl.softmax_scale,
-                              rows=[int(t)])
-        done.append(int(t))
-        if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
-            break
+    with limit:
+        for t in rows:
+            O.index_select_attend(wl.oracle_indexer(), wl.q, wl.oracle_kv(), wl.oracle_seq(), K, wl.softmax_scale,
+                                  rows=[int(t)])
+            done.append(int(t))
+            if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
+                break
     el = time.perf_counter() - t0
     vis_done = float(sum(int(wl.q_pos[t]) + 1 for t in done))
     vis_all = float((wl.q_pos.astype("int64") + 1).sum())
@@ -434,22 +467,23 @@ def main():
 
     roofline = None
     if breakdown:
-        dom = max(("index_scores", "sparse_mla"), key=lambda n: breakdown[n])
+        # the dominant one of the two entry points the timed step runs
+        dom = max(("index_topk", "sparse_mla"), key=lambda n: breakdown[n])
         by, fl = work[dom]
         us = breakdown[dom]
-        if decode:
+        bound, peak, unit = roofline_peak(wl, dom)
+        if bound == "hbm":
             achieved = by / (us * 1e-6) / 1e9
-            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic(args.workload, dom),
+            roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload, dom),
                         "algorithmic_bytes": by, "avg_us": us}
         else:
-            peak = FP8_PEAK_TFLOPS if dom == "index_scores" else BF16_PEAK_TFLOPS
             achieved = fl / (us * 1e-6) / 1e12
-            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                        "traffic": measured_traffic(args.workload, dom),
+            roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload, dom),
                         "algorithmic_flops": fl, "avg_us": us}
+        if dom == "index_topk":
+            roofline["index_topk_method"] = breakdown.get("index_topk_method")
 
     if args.copy_probe:
         # calibration for the HBM byte counters: one elementwise copy of known size

@@ -27,6 +27,16 @@ static int hip_fail(hipError_t e) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A C caller may store any integer in a sia_dtype field; reading an
+// out-of-range value through the C++ enum type is undefined, so the field is
+// read as its raw integer and range-checked before any other use.
+static bool dtype_known(const sia_dtype& d) {
+  int32_t v;
+  static_assert(sizeof(sia_dtype) == sizeof(int32_t), "sia_dtype is a 32-bit enum");
+  std::memcpy(&v, &d, sizeof v);
+  return v >= SIA_F32 && v <= SIA_MXFP8_E4M3;
+}
+
 static int check_seq(const sia_seqmap* s) {
   if (!s) return SIA_ERR_INVALID_ARG;
   if (s->num_tokens < 0) return SIA_ERR_INVALID_ARG;
@@ -43,6 +53,7 @@ static int check_seq(const sia_seqmap* s) {
 // work (num_tokens > 0).
 static int check_indexer(const sia_indexer_in* in, int num_tokens = 1) {
   if (!in) return SIA_ERR_INVALID_ARG;
+  if (!dtype_known(in->dtype)) return SIA_ERR_UNSUPPORTED;
   if (in->heads < 1 || in->dim < 1) return SIA_ERR_INVALID_ARG;
   const bool data = num_tokens > 0;
   if (data && (!in->q || !in->w || !in->k_pool)) return SIA_ERR_INVALID_ARG;
@@ -78,6 +89,7 @@ static int check_scores(const float* scores, int64_t ld, const sia_seqmap* s) {
 
 static int check_kv(const sia_kv_in* kv, sia_dtype q_dtype, int heads, int K) {
   if (!kv || !kv->kv_pool) return SIA_ERR_INVALID_ARG;
+  if (!dtype_known(kv->dtype)) return SIA_ERR_UNSUPPORTED;
   if (K < 1) return SIA_ERR_INVALID_ARG;
   if (kv->latent_dim < 1 || kv->rope_dim < 0) return SIA_ERR_INVALID_ARG;
   if (kv->dtype == SIA_F32) {
@@ -129,7 +141,6 @@ static int index_topk_auto(const sia_indexer_in& in, const sia_seqmap& seq) {
   return seq.num_tokens <= 2 * seq.batch && wgs >= num_cus() ? SIA_INDEX_TOPK_ONCHIP : SIA_INDEX_TOPK_SCORES;
 }
 
-// Workspace of either method: candidate lists (scores, positions) or the score matrix.
 // Workspace of either method: quantized queries (used when the caller passes
 // bf16 queries; sized for the largest supported indexer, 64 heads x 128), then
 // candidate lists (scores, positions) or the score matrix.
@@ -217,6 +228,7 @@ int sia_index_scores(const sia_indexer_in* in, const sia_seqmap* seq, float* sco
   rc = check_scores(scores, ld, seq);
   if (rc) return rc;
   if (in->q_bf16) return SIA_ERR_UNSUPPORTED;   // quantize first (sia_quantize_indexer_q)
+  if (seq->num_tokens == 0) return SIA_OK;
   const hipError_t e = launch_index_scores(*in, seq_args(*seq), scores, ld, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);
 }
@@ -328,10 +340,12 @@ int sia_index_topk(const sia_indexer_in* in, const sia_seqmap* seq, int32_t K, i
 int sia_quantize_indexer_q(const sia_indexer_in* in, int32_t num_tokens, void* q_codes, void* q_scales,
                            hipStream_t stream) {
   if (!in || !in->q || in->q_bf16 != 1 || num_tokens < 0 || !q_codes || !q_scales) return SIA_ERR_INVALID_ARG;
+  if (!dtype_known(in->dtype)) return SIA_ERR_UNSUPPORTED;
   if (in->dtype != SIA_FP8_E4M3 && in->dtype != SIA_MXFP8_E4M3) return SIA_ERR_UNSUPPORTED;
   if ((in->heads != 32 && in->heads != 64) || in->dim != 128) return SIA_ERR_UNSUPPORTED;
   if (!aligned16(in->q) || !aligned16(q_codes) || (reinterpret_cast<uintptr_t>(q_scales) & 3u))
     return SIA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return SIA_OK;
   const hipError_t e = launch_quantize_q(in->q, num_tokens, in->heads, in->dim, in->dtype == SIA_MXFP8_E4M3,
                                          static_cast<uint8_t*>(q_codes), q_scales, stream);
   return e == hipSuccess ? SIA_OK : hip_fail(e);

@@ -7,6 +7,7 @@ is missing or the tensors are not on a GPU, calls fail loudly.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -108,6 +109,14 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for buffers a call creates (outputs, workspace): they
+    are allocated on the launch stream, so the caching allocator hands a freed
+    workspace only to later work on that same stream, never to another stream
+    while the library's kernels may still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return SIA_F32
@@ -199,7 +208,8 @@ def index_scores(ix: Indexer, seq: SeqMap, scores: torch.Tensor = None, ld: int 
     T = seq.num_tokens
     if scores is None:
         ld = ld or (seq.max_visible + 3) // 4 * 4
-        scores = torch.empty(T, ld, dtype=torch.float32, device=ix.q.device)
+        with _on(stream):
+            scores = torch.empty(T, ld, dtype=torch.float32, device=ix.q.device)
     ld = scores.shape[1] if ld is None else ld
     a, s = ix.c(), seq.c()
     _check(lib().sia_index_scores(ctypes.byref(a), ctypes.byref(s), _ptr(scores), ld, _stream(stream)))
@@ -209,10 +219,11 @@ def index_scores(ix: Indexer, seq: SeqMap, scores: torch.Tensor = None, ld: int 
 def topk(scores: torch.Tensor, seq: SeqMap, K: int, order: int = 0, idx=None, vals=None, with_vals=False,
          stream=None):
     T = seq.num_tokens
-    if idx is None:
-        idx = torch.empty(T, K, dtype=torch.int32, device=scores.device)
-    if with_vals and vals is None:
-        vals = torch.empty(T, K, dtype=torch.float32, device=scores.device)
+    with _on(stream):
+        if idx is None:
+            idx = torch.empty(T, K, dtype=torch.int32, device=scores.device)
+        if with_vals and vals is None:
+            vals = torch.empty(T, K, dtype=torch.float32, device=scores.device)
     s = seq.c()
     _check(lib().sia_topk(_ptr(scores), scores.shape[1], ctypes.byref(s), K, order, _ptr(idx), _ptr(vals),
                           _stream(stream)))
@@ -224,11 +235,12 @@ def topk_pages(scores: torch.Tensor, seq: SeqMap, K: int, idx=None, vals=None, w
     """Block-aligned selection (sia_topk_pages): whole 64-position pages ranked by
     their best visible score, positions in ascending order, -1 padding."""
     T = seq.num_tokens
-    if idx is None:
-        idx = torch.empty(T, K, dtype=torch.int32, device=scores.device)
-    if with_vals and vals is None:
-        vals = torch.empty(T, K, dtype=torch.float32, device=scores.device)
-    ws = _workspace(ws, workspace_size(OP_TOPK_PAGES, seq, K, 1, 1), scores.device)
+    with _on(stream):
+        if idx is None:
+            idx = torch.empty(T, K, dtype=torch.int32, device=scores.device)
+        if with_vals and vals is None:
+            vals = torch.empty(T, K, dtype=torch.float32, device=scores.device)
+        ws = _workspace(ws, workspace_size(OP_TOPK_PAGES, seq, K, 1, 1), scores.device)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     s = seq.c()
     _check(lib().sia_topk_pages(_ptr(scores), scores.shape[1], ctypes.byref(s), K, _ptr(idx), _ptr(vals), _ptr(ws),
@@ -242,11 +254,12 @@ def index_topk(ix: Indexer, seq: SeqMap, K: int, order: int = 0, method: int = 0
     (order SELECT_PAGES: as topk_pages).  method: INDEX_TOPK_AUTO, INDEX_TOPK_ONCHIP or INDEX_TOPK_SCORES."""
     T = seq.num_tokens
     dev = ix.q.device
-    if idx is None:
-        idx = torch.empty(T, K, dtype=torch.int32, device=dev)
-    if with_vals and vals is None:
-        vals = torch.empty(T, K, dtype=torch.float32, device=dev)
-    ws = _workspace(ws, workspace_size(OP_INDEX_TOPK, seq, K, 1, 1), dev)
+    with _on(stream):
+        if idx is None:
+            idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+        if with_vals and vals is None:
+            vals = torch.empty(T, K, dtype=torch.float32, device=dev)
+        ws = _workspace(ws, workspace_size(OP_INDEX_TOPK, seq, K, 1, 1), dev)
     a, s = ix.c(), seq.c()
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().sia_index_topk(ctypes.byref(a), ctypes.byref(s), K, order, method, _ptr(idx), _ptr(vals), _ptr(ws),
@@ -259,11 +272,12 @@ def quantize_indexer_q(ix: Indexer, stream=None):
     fp8 keys, uint8 E8M0 [T, Hi, Di/32] for MXFP8 keys."""
     a = ix.c()
     T, Hi, Di = ix.q.shape
-    codes = torch.empty(T, Hi, Di, dtype=torch.uint8, device=ix.q.device)
-    if a.dtype == SIA_MXFP8_E4M3:
-        scales = torch.empty(T, Hi, Di // 32, dtype=torch.uint8, device=ix.q.device)
-    else:
-        scales = torch.empty(T, dtype=torch.float32, device=ix.q.device)
+    with _on(stream):
+        codes = torch.empty(T, Hi, Di, dtype=torch.uint8, device=ix.q.device)
+        if a.dtype == SIA_MXFP8_E4M3:
+            scales = torch.empty(T, Hi, Di // 32, dtype=torch.uint8, device=ix.q.device)
+        else:
+            scales = torch.empty(T, dtype=torch.float32, device=ix.q.device)
     _check(lib().sia_quantize_indexer_q(ctypes.byref(a), T, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
@@ -278,10 +292,11 @@ def index_topk_method(ix: Indexer, seq: SeqMap) -> str:
 
 def _mla(fn, op, q, kv: LatentKV, seq: SeqMap, idx, K, softmax_scale, out, lse, ws, stream):
     T, H = q.shape[0], q.shape[1]
-    if out is None:
-        out = torch.empty(T, H, kv.latent_dim, dtype=q.dtype, device=q.device)
     n = workspace_size(op, seq, K, H, kv.latent_dim) if kv.pool.dtype != torch.float32 else 0
-    ws = _workspace(ws, n, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(T, H, kv.latent_dim, dtype=q.dtype, device=q.device)
+        ws = _workspace(ws, n, q.device)
     s, k = seq.c(), kv.c()
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(fn(_ptr(q), dtype_code(q), H, ctypes.byref(k), ctypes.byref(s), _ptr(idx), K, float(softmax_scale),
@@ -304,10 +319,11 @@ def sparse_mla_prefill(q, kv: LatentKV, seq: SeqMap, idx, K, softmax_scale, out=
 def index_select_attend(ix: Indexer, q, kv: LatentKV, seq: SeqMap, K, softmax_scale, order=0, idx_out=None,
                         out=None, lse=None, ws=None, stream=None):
     T, H = q.shape[0], q.shape[1]
-    if out is None:
-        out = torch.empty(T, H, kv.latent_dim, dtype=q.dtype, device=q.device)
     n = workspace_size(OP_INDEX_SELECT_ATTEND, seq, K, H, kv.latent_dim)
-    ws = _workspace(ws, n, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(T, H, kv.latent_dim, dtype=q.dtype, device=q.device)
+        ws = _workspace(ws, n, q.device)
     a, s, k = ix.c(), seq.c(), kv.c()
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().sia_index_select_attend(ctypes.byref(a), _ptr(q), dtype_code(q), H, ctypes.byref(k),

@@ -48,6 +48,9 @@ CONFIGS = {
     # 16 sequences x 131072 context, fp8 latent KV with one scale per 64-token page
     "quant_decode": dict(cid=3, kind="decode", B=16, ctx=131072, Hi=64, Di=128, idx_dtype="fp8",
                          K=2048, H=128, Dc=512, Dr=64, kv_dtype="fp8", kv_scale=(64, 512)),
+    # the same with the pages' KV tiling: one fp32 scale per token and 128-element tile
+    "quant_decode_tile128": dict(cid=3, kind="decode", B=16, ctx=131072, Hi=64, Di=128, idx_dtype="fp8",
+                                 K=2048, H=128, Dc=512, Dr=64, kv_dtype="fp8", kv_scale=(1, 128)),
     # rank 0 of a 16-way zigzag split of a 262144-token prefix: segments 0 and 31 of 32
     "cp_chunk_prefill": dict(cid=4, kind="zigzag", total=262144, segments=32, rank=0,
                              Hi=64, Di=128, idx_dtype="fp8", K=2048, H=128, Dc=512, Dr=64,
@@ -375,16 +378,31 @@ def make_workload(name: str, mla=True, indexer=True, overrides=None) -> Workload
     return wl
 
 
-def sample_rows(wl: Workload, n: int, K: int) -> np.ndarray:
-    """Deterministic sample of query rows: first 8, last 8, rows around q_pos = K-1,
-    and evenly spaced rows in between."""
+def sample_rows(wl: Workload, n: int, K: int, boundary: int = 8192) -> np.ndarray:
+    """Deterministic sample of query rows for full-size checks.
+
+    Always holds: the first two and last two rows; the rows at q_pos = K-2..K
+    (where a row starts to see more than K keys); the first three rows after
+    every jump of q_pos inside a sequence (the start of a zigzag segment) and
+    the row before it; for every multiple m of `boundary` (the key ranges and
+    page chunks of the indexer kernels) the first rows at q_pos = m-1 and m;
+    plus max(n - those, n // 2) rows evenly spaced over the whole batch."""
     Tq = wl.Tq
     if Tq <= n:
         return np.arange(Tq)
-    s = set(range(8)) | set(range(Tq - 8, Tq))
-    near = np.nonzero(np.abs(wl.q_pos.astype(np.int64) - (K - 1)) <= 2)[0]
-    s |= set(int(x) for x in near[:6])
-    rest = n - len(s)
-    if rest > 0:
-        s |= set(int(x) for x in np.linspace(0, Tq - 1, rest + 2)[1:-1].round())
-    return np.array(sorted(s))[: max(n, 16)]
+    pos = wl.q_pos.astype(np.int64)
+    seq = wl.q_seq.astype(np.int64)
+    s = {0, 1, Tq - 2, Tq - 1}
+    s |= set(int(x) for x in np.nonzero(np.abs(pos - (K - 1)) <= 1)[0][:3])
+    jumps = np.nonzero((seq[1:] == seq[:-1]) & (pos[1:] - pos[:-1] > 1))[0]
+    for j in jumps[:8]:
+        s |= {int(j), int(j) + 1, int(j) + 2, int(j) + 3}
+    if len(np.unique(pos)) > 1:
+        for m in range(boundary, int(pos.max()) + 2, boundary):
+            for want in (m - 1, m):
+                hit = np.nonzero(pos == want)[0]
+                if hit.size:
+                    s.add(int(hit[0]))
+    rest = max(n - len(s), n // 2)
+    s |= set(int(x) for x in np.linspace(0, Tq - 1, rest + 2)[1:-1].round())
+    return np.array(sorted(x for x in s if 0 <= x < Tq))

@@ -11,13 +11,11 @@ import oracle as O
 from sparse_index_attention_amd import sia
 from sparse_index_attention_amd import workloads as W
 
-# Score tolerance: |g - o| <= 1e-3 |o| + eps * A, with A the same score computed
-# on absolute values (sum_h |w_h| qs ks sum_d |q_hd k_sd|), i.e. the magnitude
-# that bounds any summation-order or accumulator-rounding error.  eps is 2^-11
-# for the fp8 MFMA path (its internal accumulation rounds at ~2^-14 of A) and
-# 2^-16 for the fp32 path.
+# Score tolerance (the stated "1e-3 relative"): |g - o| <= 1e-3 |o| + 1e-6 max_s |o[t, s]|
+# per row.  The floor only matters for exact and near-exact zeros (ReLU), where
+# a different summation order may flip the sign of a head's dot product.
 SCORE_REL = 1e-3
-SCORE_EPS = {"fp8": 2.0 ** -11, "mxfp8": 2.0 ** -11, "bf16": 2.0 ** -16, "f32": 2.0 ** -16}
+SCORE_FLOOR = 1e-6
 # Attention tolerance: |g - o| <= ATOL + RTOL |o| elementwise.
 ATT_TOL = {"bf16": (2e-2, 1e-2), "fp8": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
 LSE_ATOL = {"bf16": 2e-2, "fp8": 2e-2, "f32": 1e-4}
@@ -50,7 +48,9 @@ def upload(wl: W.Workload, device="cuda"):
 
 
 def score_bound_row(wl: W.Workload, t: int) -> np.ndarray:
-    """A[t, s] for s <= q_pos[t] (see SCORE_EPS)."""
+    """A[t, s] for s <= q_pos[t]: the score taken on absolute values,
+    sum_h |w_h| qs ks sum_d |q_hd k_sd|, the magnitude any summation-order or
+    accumulator rounding error scales with (reported, not asserted)."""
     idx = wl.oracle_indexer()
     b, pos = int(wl.q_seq[t]), int(wl.q_pos[t])
     slots = O.physical_slots(wl.block_table[b], np.arange(pos + 1), W.PAGE)
@@ -68,19 +68,40 @@ def score_bound_row(wl: W.Workload, t: int) -> np.ndarray:
     return O.index_scores_row(np.abs(qv), qs, np.abs(idx["w"][t].astype(np.float64)), np.abs(keys), ks)
 
 
-def check_scores(wl, rows, got: np.ndarray, exp: dict):
-    eps = SCORE_EPS[wl.cfg["idx_dtype"]]
-    worst = 0.0
+def check_scores(wl, rows, got: np.ndarray, exp: dict, label=None, bound_rows=64):
+    """Assert |g - o| <= 1e-3 |o| + 1e-6 max|o| on every entry of every row and
+    print the worst observed errors: the ratio to that bound, the relative
+    error over entries above the floor, and (on up to `bound_rows` rows) the
+    error over A (score_bound_row)."""
+    worst_ratio, worst_rel, worst_a, n = 0.0, 0.0, 0.0, 0
+    first_bad = None
     for i, t in enumerate(rows):
-        n = int(wl.q_pos[t]) + 1
+        n_vis = int(wl.q_pos[t]) + 1
         o = exp[t].astype(np.float64)
-        g = got[i, :n].astype(np.float64)
-        tol = SCORE_REL * np.abs(o) + eps * score_bound_row(wl, t)
+        g = got[i, :n_vis].astype(np.float64)
+        floor = SCORE_FLOOR * float(np.max(np.abs(o)))
         err = np.abs(g - o)
+        tol = SCORE_REL * np.abs(o) + floor
+        ratio = err / np.maximum(tol, 1e-300)
         bad = np.nonzero(~(err <= tol))[0]
-        assert bad.size == 0, f"row {t}: {bad.size} scores out of tolerance, first s={bad[0]} g={g[bad[0]]} o={o[bad[0]]}"
-        worst = max(worst, float(np.max(err / np.maximum(tol, 1e-30))))
-    return worst
+        if bad.size and first_bad is None:
+            first_bad = (t, bad.size, int(bad[0]), g[bad[0]], o[bad[0]])
+        worst_ratio = max(worst_ratio, float(np.max(ratio)))
+        big = np.abs(o) > floor
+        if big.any():
+            worst_rel = max(worst_rel, float(np.max(err[big] / np.abs(o[big]))))
+        if i < bound_rows:
+            A = score_bound_row(wl, t)
+            pos = A > 0
+            if pos.any():
+                worst_a = max(worst_a, float(np.max(err[pos] / A[pos])))
+        n += n_vis
+    name = label or wl.name
+    print(f"[score-err] {name} ({wl.cfg['idx_dtype']}): {n} scores; worst |g-o|/bound {worst_ratio:.3g}, "
+          f"worst |g-o|/|o| {worst_rel:.3g}, worst |g-o|/A {worst_a:.3g}", flush=True)
+    assert first_bad is None, (f"row {first_bad[0]}: {first_bad[1]} scores beyond 1e-3|o| + 1e-6 max|o|, "
+                               f"first s={first_bad[2]} g={first_bad[3]} o={first_bad[4]}")
+    return worst_ratio
 
 
 def check_attention(kind, got_out, got_lse, exp: dict, rows):

@@ -20,8 +20,10 @@ from gpu_support import check_attention, check_scores, dev, kind_of, page_band_o
 
 pytestmark = pytest.mark.gpu
 
-# name -> number of sampled query rows
-CASES = {"decode": 6, "quant_decode": 3, "long_prefill": 10, "cp_chunk_prefill": 8, "mx_decode": 3, "bf16_decode": 3}
+# name -> number of sampled query rows asked of sample_rows (it adds range
+# boundaries, segment edges and the rows around q_pos = K-1 to these)
+CASES = {"decode": 8, "quant_decode": 4, "quant_decode_tile128": 4, "long_prefill": 24, "cp_chunk_prefill": 24,
+         "mx_decode": 3, "bf16_decode": 3}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -45,11 +47,8 @@ def test_full_size(name):
     wl = W.make_workload(name)
     K, H = wl.cfg["K"], wl.cfg["H"]
     rows = W.sample_rows(wl, CASES[name], K)
-    if len(rows) > CASES[name]:
-        # keep the extremes and an even spread
-        pick = np.unique(np.linspace(0, len(rows) - 1, CASES[name]).round().astype(int))
-        rows = rows[pick]
-    print(f"[full] {name}: uploading; sampled rows {list(rows)}", flush=True)
+    print(f"[full] {name}: uploading; {len(rows)} sampled rows {[int(r) for r in rows]}, "
+          f"q_pos {[int(p) for p in wl.q_pos[rows]]}", flush=True)
     seq, ix, q, kv = upload(wl)
 
     # fused path, as benchmarked
@@ -91,7 +90,7 @@ def test_full_size(name):
     g_sc = g_sc.cpu().numpy()
 
     sc = O.index_scores(wl.oracle_indexer(), wl.oracle_seq(), [int(t) for t in rows])
-    check_scores(wl, [int(t) for t in rows], g_sc, sc)
+    check_scores(wl, [int(t) for t in rows], g_sc, sc, label=f"{name} (full size)", bound_rows=4)
 
     # Top-K fed the oracle's scores: bit-exact
     buf = np.full((len(rows), ld), np.nan, dtype=np.float32)
@@ -141,9 +140,6 @@ def test_full_size_page_selection(name):
     wl = W.make_workload(name)
     K, H = wl.cfg["K"], wl.cfg["H"]
     rows = W.sample_rows(wl, PAGE_CASES[name], K)
-    if len(rows) > PAGE_CASES[name]:
-        pick = np.unique(np.linspace(0, len(rows) - 1, PAGE_CASES[name]).round().astype(int))
-        rows = rows[pick]
     print(f"[full-pages] {name}: sampled rows {list(rows)}", flush=True)
     seq, ix, q, kv = upload(wl)
     idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
