@@ -19,7 +19,8 @@
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers (HIP device memory), row-major with
  *     the last dimension contiguous, owned by the caller.  The library never
- *     allocates, frees or keeps a pointer after returning.
+ *     allocates, frees or keeps a pointer after returning.  (The one device
+ *     array it holds is the workspace of sia_index_select_attend_noalloc.)
  *   - Work is enqueued asynchronously on `stream`; nothing synchronizes the host.
  *     The caller synchronizes before reading outputs.
  *   - Arguments are validated on the host before anything is launched.  On a
@@ -28,7 +29,8 @@
  *   - Device-resident metadata (q_pos, q_seq, block tables, indices) cannot be
  *     checked on the host.  The kernels clamp it so that no access leaves its
  *     buffer, but values outside the documented ranges give unspecified results.
- *   - The library keeps no mutable global state; calls are thread-safe.
+ *   - Calls are thread-safe.  The only global state is the per-GPU address of
+ *     the sia_index_select_attend_noalloc workspace, looked up under a lock.
  *   - fp8 is OCP e4m3fn (bias 7, max 448, no infinities), gfx950's native format.
  *   - Dequantization scales must be finite and > 0.
  */
@@ -272,6 +274,25 @@ int sia_index_select_attend(const sia_indexer_in* in, const void* q_mla, sia_dty
                             int32_t heads, const sia_kv_in* kv, const sia_seqmap* seq, int32_t K,
                             int32_t order, float softmax_scale, int32_t* idx_out, void* out,
                             float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole path in one call without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments and results are those of
+ * sia_index_select_attend.  The workspace is a device array inside the
+ * library, SIA_NOALLOC_WORKSPACE_BYTES per GPU, allocated when the library's
+ * code is loaded on that GPU and held until the process ends; the call itself
+ * allocates nothing.  A call whose sia_workspace_size(SIA_OP_INDEX_SELECT_ATTEND,
+ * ...) exceeds that size returns SIA_ERR_WORKSPACE before anything is
+ * launched (decode batches fit: 64 sequences x 32768 tokens need 41.2 MiB;
+ * long prefills, whose score matrix is T x max_visible floats, do not).  Every
+ * call on one GPU uses that GPU's array: calls that may overlap on one GPU
+ * (different streams without ordering between them) race and must be
+ * serialized by the caller.  Nothing in the array needs to start cleared.     */
+#define SIA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int sia_index_select_attend_noalloc(const sia_indexer_in* in, const void* q_mla, sia_dtype q_dtype,
+                                    int32_t heads, const sia_kv_in* kv, const sia_seqmap* seq, int32_t K,
+                                    int32_t order, float softmax_scale, int32_t* idx_out, void* out,
+                                    float* lse, hipStream_t stream);
 
 /* Bytes of workspace `op` needs for this sequence map, K, heads and latent
  * dimension (0 when none).  Returns (size_t)-1 for invalid arguments.          */

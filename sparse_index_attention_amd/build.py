@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsia.so")
-SOURCES = ["indexer.hip", "indexer_bf16.hip", "topk.hip", "topk_pages.hip", "index_topk.hip", "quantize.hip", "sparse_mla.hip", "sia_api.cpp"]
+SOURCES = ["indexer.hip", "indexer_bf16.hip", "topk.hip", "topk_pages.hip", "index_topk.hip", "quantize.hip", "sparse_mla.hip", "noalloc.hip", "sia_api.cpp"]
 # per-source extra flags (none needed at present)
 SOURCE_FLAGS = {}
 

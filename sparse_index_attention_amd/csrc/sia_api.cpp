@@ -20,10 +20,11 @@ int num_cus() {
   return n;
 }
 
-static int hip_fail(hipError_t e) {
+int record_hip_error(hipError_t e) {
   g_last_hip_error = hipGetErrorString(e);
   return SIA_ERR_HIP;
 }
+static int hip_fail(hipError_t e) { return record_hip_error(e); }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

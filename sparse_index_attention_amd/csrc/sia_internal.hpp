@@ -24,6 +24,8 @@ inline SeqArgs seq_args(const sia_seqmap& s) {
 }
 
 int num_cus();
+// Records e as the text sia_last_hip_error returns; gives SIA_ERR_HIP.
+int record_hip_error(hipError_t e);
 
 // indexer.hip
 hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float* scores, int64_t ld,

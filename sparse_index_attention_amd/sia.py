@@ -71,13 +71,15 @@ def lib():
         L.sia_sparse_mla_prefill.argtypes = mla
         L.sia_index_select_attend.argtypes = [P(IndexerC), c_p, ctypes.c_int, c_i32, P(KvC), P(SeqMapC), c_i32,
                                               c_i32, ctypes.c_float, c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]
+        L.sia_index_select_attend_noalloc.argtypes = [P(IndexerC), c_p, ctypes.c_int, c_i32, P(KvC), P(SeqMapC),
+                                                      c_i32, c_i32, ctypes.c_float, c_p, c_p, c_p, c_p]
         L.sia_workspace_size.argtypes = [c_i32, P(SeqMapC), c_i32, c_i32, c_i32]
         L.sia_workspace_size.restype = ctypes.c_size_t
         L.sia_status_string.argtypes = [ctypes.c_int]
         L.sia_status_string.restype = ctypes.c_char_p
         L.sia_last_hip_error.restype = ctypes.c_char_p
         for f in ("sia_index_scores", "sia_topk", "sia_sparse_mla_decode", "sia_sparse_mla_prefill",
-                  "sia_index_select_attend"):
+                  "sia_index_select_attend", "sia_index_select_attend_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -329,4 +331,24 @@ def index_select_attend(ix: Indexer, q, kv: LatentKV, seq: SeqMap, K, softmax_sc
     _check(lib().sia_index_select_attend(ctypes.byref(a), _ptr(q), dtype_code(q), H, ctypes.byref(k),
                                          ctypes.byref(s), K, order, float(softmax_scale), _ptr(idx_out),
                                          _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20   # SIA_NOALLOC_WORKSPACE_BYTES
+
+
+def index_select_attend_noalloc(ix: Indexer, q, kv: LatentKV, seq: SeqMap, K, softmax_scale, order=0, idx_out=None,
+                                out=None, lse=None, stream=None):
+    """index_select_attend without a workspace: the library uses its own
+    per-GPU device array (SIA_NOALLOC_WORKSPACE_BYTES) and allocates nothing.
+    Pass `out` (and `idx_out`, `lse`) to keep the whole call allocation-free;
+    calls that may overlap on one GPU must be serialized by the caller."""
+    T, H = q.shape[0], q.shape[1]
+    if out is None:
+        with _on(stream):
+            out = torch.empty(T, H, kv.latent_dim, dtype=q.dtype, device=q.device)
+    a, s, k = ix.c(), seq.c(), kv.c()
+    _check(lib().sia_index_select_attend_noalloc(ctypes.byref(a), _ptr(q), dtype_code(q), H, ctypes.byref(k),
+                                                 ctypes.byref(s), K, order, float(softmax_scale), _ptr(idx_out),
+                                                 _ptr(out), _ptr(lse), _stream(stream)))
     return out

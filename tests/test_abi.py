@@ -239,3 +239,29 @@ def test_zero_tokens_is_a_noop(Lcpu):
     L = Lcpu
     seq = good_seq(num_tokens=0)
     assert call_scores(L, good_indexer(), seq) == 0
+
+
+def test_noalloc_rejects_workspaces_beyond_its_array(Lcpu):
+    """sia_index_select_attend_noalloc validates like sia_index_select_attend
+    and returns SIA_ERR_WORKSPACE, before touching the device, for a call
+    whose workspace would exceed the library's array (a long prefill's score
+    matrix); invalid arguments keep their own status."""
+    L = Lcpu
+    kv = sia.KvC(FAKE, 0, sia.SIA_BF16, 64, 512, 512, 64)
+    ix = good_indexer()
+
+    def f(seq, K=2048, heads=128, order=0, kvs=kv):
+        return L.sia_index_select_attend_noalloc(ctypes.byref(ix), ctypes.c_void_p(FAKE), sia.SIA_BF16, heads,
+                                                 ctypes.byref(kvs), ctypes.byref(seq), K, order, 0.04,
+                                                 ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, None)
+    prefill = good_seq(num_tokens=65536, batch=1, max_pages=1024, num_pages=1024, max_visible=65536)
+    n = L.sia_workspace_size(sia.OP_INDEX_SELECT_ATTEND, ctypes.byref(prefill), 2048, 128, 512)
+    assert n > sia.NOALLOC_WORKSPACE_BYTES
+    assert f(prefill) == -3
+    assert f(prefill, heads=96) == -2
+    assert f(prefill, order=5) == -1
+    assert f(good_seq(page_size=32)) == -2
+    assert f(good_seq(num_tokens=0)) == 0
+    decode = good_seq(num_tokens=64, batch=64, max_pages=512, num_pages=32768, max_visible=32768)
+    assert L.sia_workspace_size(sia.OP_INDEX_SELECT_ATTEND, ctypes.byref(decode), 2048, 128, 512) \
+        <= sia.NOALLOC_WORKSPACE_BYTES
