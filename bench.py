@@ -63,9 +63,11 @@ TRAFFIC_KERNELS = {                 # roofline kernel -> (kernel-name substrings
                    ("sparse_mla.hip", "sia_common.hpp", "sia_internal.hpp")),
     "index_scores": (("k_index_scores_fp8",),
                      ("indexer.hip", "index_core.hpp", "block_prims.hpp", "sia_common.hpp", "sia_internal.hpp")),
-    "index_topk": (("k_index_topk_ranges", "k_topk"),
-                   ("index_topk.hip", "topk.hip", "index_core.hpp", "block_prims.hpp", "sia_common.hpp",
-                    "sia_internal.hpp")),
+    # the fused call's steps 1 + 2: the on-chip method (ranges + candidate Top-K) or
+    # the score-matrix method (scores + Top-K); count with --no-breakdown
+    "index_topk": (("k_index_topk_ranges", "k_index_scores_fp8", "k_topk"),
+                   ("index_topk.hip", "indexer.hip", "topk.hip", "index_core.hpp", "block_prims.hpp",
+                    "sia_common.hpp", "sia_internal.hpp")),
 }
 
 

@@ -30,8 +30,10 @@
 // gfx950's 64 four-byte LDS banks.
 //
 // Decode splits a token's rows over several workgroups; each writes a partial
-// (O normalised over its rows, LSE) and a combine kernel merges them with
-// softmax weights exp(lse_s - LSE) in a fixed order.
+// (O normalised over its rows, rounded to bf16, and its LSE in float) and a
+// combine kernel merges them with softmax weights exp(lse_s - LSE) in a fixed
+// order.  The merge is a convex combination, so the bf16 partials add at most
+// one more rounding of 2^-9 relative to the output's own.
 #include "sia_common.hpp"
 #include "sia_internal.hpp"
 
@@ -52,8 +54,8 @@ struct MlaArgs {
   int rows_per_split;
   void* out;    // final output (splits == 1)
   float* lse;   // nullable
-  float* ws_o;  // [T, splits, H, Dc] partial outputs (splits > 1)
-  float* ws_lse;
+  uint16_t* ws_o;  // [T, splits, H, Dc] bf16 partial outputs (splits > 1)
+  float* ws_lse;    // [T, splits, H]
 };
 
 // ---------------------------------------------------------------------------
@@ -605,14 +607,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     if (a.lse && hh == 0 && ch == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
   } else {
     const int64_t pidx = ((int64_t)t * a.splits + split) * a.H + head;
-    float* po = a.ws_o + pidx * kDc + vc0;
+    uint16_t* po = a.ws_o + pidx * kDc + vc0;
 #pragma unroll
     for (int vt = 0; vt < kVT; ++vt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int vc = 32 * vt + 8 * q4 + 4 * hh;
-        *(float4*)(po + vc) = make_float4(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv, o[vt][4 * q4 + 2] * inv,
-                                          o[vt][4 * q4 + 3] * inv);
+        uint2 w;
+        w.x = pack_bf16x2(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv);
+        *(uint2*)(po + vc) = w;
       }
     if (hh == 0 && ch == 0) a.ws_lse[pidx] = lse_v;
   }
@@ -634,18 +638,14 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
   const int S = a.splits;
   const int64_t hstride = (int64_t)a.H * kDc;  // between the partials of consecutive splits
   const float* __restrict__ lse_t = a.ws_lse + (int64_t)t * S * a.H + h;
-  const float* __restrict__ o_t = a.ws_o + ((int64_t)t * S * a.H + h) * kDc + lane * 8;
+  const uint16_t* __restrict__ o_t = a.ws_o + ((int64_t)t * S * a.H + h) * kDc + lane * 8;
 
   const float ls = lane < S ? lse_t[(int64_t)lane * a.H] : -INFINITY;
-  float4 v[kCombineGroup][2];
+  uint4 v[kCombineGroup];
   auto load_group = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kCombineGroup; ++u)
-      if (g + u < S) {
-        const float4* po = reinterpret_cast<const float4*>(o_t + (g + u) * hstride);
-        v[u][0] = po[0];
-        v[u][1] = po[1];
-      }
+      if (g + u < S) v[u] = *reinterpret_cast<const uint4*>(o_t + (g + u) * hstride);
   };
   load_group(0);
   const float mx = wave_max(ls);  // exact, so every lane holds the same value
@@ -661,9 +661,12 @@ __global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a) {
       const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), g + u));
       tot += wgt;
       if (wgt != 0.f) {
-        const float x[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+        const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = fmaf(wgt, x[k], acc[k]);
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = fmaf(wgt, __uint_as_float(wd[k] << 16), acc[2 * k]);
+          acc[2 * k + 1] = fmaf(wgt, __uint_as_float(wd[k] & 0xffff0000u), acc[2 * k + 1]);
+        }
       }
     }
   }
@@ -694,7 +697,8 @@ int mla_splits(int T, int K, int heads) {
 size_t mla_workspace_bytes(int T, int K, int heads, int latent) {
   const int s = mla_splits(T, K, heads);
   if (s <= 1) return 0;
-  return (size_t)T * s * heads * ((size_t)latent + 1) * sizeof(float) + 256;
+  // bf16 partial outputs, then one float LSE per (token, split, head)
+  return (size_t)T * s * heads * ((size_t)latent * sizeof(uint16_t) + sizeof(float)) + 256;
 }
 
 hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, const SeqArgs& s, const int32_t* idx,
@@ -726,8 +730,8 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
   rps = (rps + kRowsTile - 1) / kRowsTile * kRowsTile;
   a.rows_per_split = rps;
   if (a.splits > 1) {
-    a.ws_o = (float*)ws;
-    a.ws_lse = a.ws_o + (size_t)s.T * a.splits * heads * kDc;
+    a.ws_o = (uint16_t*)ws;
+    a.ws_lse = (float*)(a.ws_o + (size_t)s.T * a.splits * heads * kDc);
   }
   const int64_t units = (int64_t)s.T * a.splits;
   const int parts = heads >= 128 ? 2 : 1;

@@ -59,6 +59,6 @@ size_t topk_pages_ws_bytes(int T, int max_visible, int K) {
 int mla_splits(int T, int K, int) { return T >= 256 ? 1 : (K + 255) / 256; }
 size_t mla_workspace_bytes(int T, int K, int heads, int latent) {
   const int s = mla_splits(T, K, heads);
-  return s <= 1 ? 0 : (size_t)T * s * heads * ((size_t)latent + 1) * sizeof(float) + 256;
+  return s <= 1 ? 0 : (size_t)T * s * heads * ((size_t)latent * 2 + 4) + 256;
 }
 }  // namespace sia
