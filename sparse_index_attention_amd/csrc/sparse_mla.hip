@@ -587,38 +587,45 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   }
   }
 
-  // ---- finish: normalise and write this column half
+  // ---- finish: normalise, stage the workgroup's heads x 512 columns in LDS
+  // (the tiles are free after the pass loop's last barrier), then write each
+  // head's row with contiguous 16-byte stores, one whole 1 KB row per wave
+  // store instruction.  Stored straight from the accumulator, a store
+  // instruction would touch 32 head rows 1 KB apart with 8 bytes each.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  const int vc0 = kVH * ch;
-  if (a.splits == 1) {
-    uint16_t* out = (uint16_t*)a.out + ((int64_t)t * a.H + head) * kDc + vc0;
+  constexpr int kPitch = kDc * 2 + 16;           // staged row bytes; the pad keeps LDS writes to 2-way conflicts
+  static_assert(32 * kPitch <= kTileBytes, "a head block's rows fit one tile buffer");
+  {
+    lds_u8* srow = (hbl == 0 ? T0 : T1) + nn * kPitch + 2 * (kVH * ch);
 #pragma unroll
     for (int vt = 0; vt < kVT; ++vt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int vc = 32 * vt + 8 * q4 + 4 * hh;
-        uint2 w;
-        w.x = pack_bf16x2(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv);
-        w.y = pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv);
-        *(uint2*)(out + vc) = w;
+        const uint64_t w = (uint64_t)pack_bf16x2(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv) |
+                           ((uint64_t)pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv) << 32);
+        *(__attribute__((address_space(3))) uint64_t*)(srow + 2 * vc) = w;
       }
-    if (a.lse && hh == 0 && ch == 0) a.lse[(int64_t)t * a.H + head] = lse_v;
-  } else {
-    const int64_t pidx = ((int64_t)t * a.splits + split) * a.H + head;
-    uint16_t* po = a.ws_o + pidx * kDc + vc0;
-#pragma unroll
-    for (int vt = 0; vt < kVT; ++vt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int vc = 32 * vt + 8 * q4 + 4 * hh;
-        uint2 w;
-        w.x = pack_bf16x2(o[vt][4 * q4] * inv, o[vt][4 * q4 + 1] * inv);
-        w.y = pack_bf16x2(o[vt][4 * q4 + 2] * inv, o[vt][4 * q4 + 3] * inv);
-        *(uint2*)(po + vc) = w;
-      }
-    if (hh == 0 && ch == 0) a.ws_lse[pidx] = lse_v;
+  }
+  __syncthreads();
+  uint16_t* obase = a.splits == 1 ? (uint16_t*)a.out + (int64_t)t * a.H * kDc
+                                  : a.ws_o + ((int64_t)t * a.splits + split) * a.H * kDc;
+  const int head0 = part * HBW * 32;
+  constexpr int kRowChunks = kDc * 2 / 16;       // 16-byte chunks per output row
+#pragma unroll 4
+  for (int c = tid; c < HBW * 32 * kRowChunks; c += NT) {
+    const int r = c / kRowChunks, k = c % kRowChunks;
+    const v4i v = *(const lds_v4i*)((r < 32 ? T0 : T1) + (r & 31) * kPitch + 16 * k);
+    *(v4i*)(obase + (int64_t)(head0 + r) * kDc + 8 * k) = v;
+  }
+  if (hh == 0 && ch == 0) {
+    if (a.splits == 1) {
+      if (a.lse) a.lse[(int64_t)t * a.H + head] = lse_v;
+    } else {
+      a.ws_lse[((int64_t)t * a.splits + split) * a.H + head] = lse_v;
+    }
   }
 }
 
