@@ -167,9 +167,10 @@ def algorithmic_work(wl):
     idx_flops = float(vis.sum() * 2 * Hi * Di)
     mla_bytes = float(sel.sum() * (row_b + 4) + wl.Tq * H * ((Dc + Dr) + Dc) * elt)
     mla_flops = float(sel.sum() * 2 * H * ((Dc + Dr) + Dc))
-    topk_bytes = float(wl.Tq * K * 4)
+    # Top-K over a score matrix reads each visible score once and writes K indices
+    topk_bytes = float(vis.sum() * 4 + wl.Tq * K * 4)
     return {"index_scores": (idx_bytes, idx_flops), "topk": (topk_bytes, 0.0),
-            "index_topk": (idx_bytes + topk_bytes, idx_flops), "sparse_mla": (mla_bytes, mla_flops)}
+            "index_topk": (idx_bytes + float(wl.Tq * K * 4), idx_flops), "sparse_mla": (mla_bytes, mla_flops)}
 
 
 def roofline_peak(wl, kernel):
@@ -178,7 +179,7 @@ def roofline_peak(wl, kernel):
     MLA on the bf16 MFMA (fp8 latent rows are dequantized to bf16); the fp32
     path runs on the vector ALU."""
     c = wl.cfg
-    if c["kind"] == "decode":
+    if c["kind"] == "decode" or kernel == "topk":
         return "hbm", HBM_PEAK_GBS, "GB/s"
     dt = c["idx_dtype"] if kernel in ("index_scores", "index_topk") else c["kv_dtype"]
     if dt == "f32":
@@ -469,8 +470,14 @@ def main():
 
     roofline = None
     if breakdown:
-        # the dominant one of the two entry points the timed step runs
-        dom = max(("index_topk", "sparse_mla"), key=lambda n: breakdown[n])
+        # the dominant one of the kernels the timed step runs: steps 1 + 2 are
+        # one fused pair on chip (ranges + candidate Top-K), or two kernels
+        # through the score matrix (scores, then Top-K)
+        if breakdown["index_topk_method"] == "scores":
+            candidates = ("index_scores", "topk", "sparse_mla")
+        else:
+            candidates = ("index_topk", "sparse_mla")
+        dom = max(candidates, key=lambda n: breakdown[n])
         by, fl = work[dom]
         us = breakdown[dom]
         bound, peak, unit = roofline_peak(wl, dom)
@@ -484,7 +491,7 @@ def main():
             roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                         "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload, dom),
                         "algorithmic_flops": fl, "avg_us": us}
-        if dom == "index_topk":
+        if dom in ("index_topk", "index_scores", "topk"):
             roofline["index_topk_method"] = breakdown.get("index_topk_method")
 
     if args.copy_probe:
