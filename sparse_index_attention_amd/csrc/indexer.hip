@@ -143,10 +143,25 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
   const int pos = has_q ? clampi(a.s.q_pos[t], -1, a.s.max_visible - 1) : -1;
   const int my_seq = has_q ? clampi(a.s.q_seq[t], 0, a.s.batch - 1) : -1;
   const int c_own = (pos >> 6) + 1;
-  const __amdgpu_buffer_rsrc_t srs =
-      __builtin_amdgcn_make_buffer_rsrc(a.scores + (int64_t)(has_q ? t : 0) * a.ld, 0, a.s.max_visible * 4, kRawBuffer);
+  float* const srow = a.scores + (int64_t)(has_q ? t : 0) * a.ld;
   const uint8_t* __restrict__ kpool = (const uint8_t*)a.k_pool;
   const int sr = tid >> 2, sj = 2 * (tid & 3);  // thread moves row sr, chunks sj and sj+1
+  // Per-lane parts of every address are fixed for the whole kernel; the
+  // per-page parts are wave-uniform and go into buffer descriptors built with
+  // scalar arithmetic, so the page loop spends its vector instructions on the
+  // scores themselves.
+  const int kvoff = sr * 128 + 16 * sj;    // this thread's bytes of a key page
+  // LDS read bases of the key operand: key row 32kt + nn (kt adds 4096 bytes),
+  // 16-byte chunk j at j ^ ((row >> 1) & 7), the same swizzle for both kt
+  int kbase[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      // 16-byte chunks of the row this lane feeds (see mx_operand for MX)
+      const int j = MX ? 4 * st + 2 * x + hh : 4 * hh + 2 * st + x;
+      kbase[st][x] = kswz(nn, j);
+    }
 
   // ---- this wave's query (operand A) and folded head weights
   v8i qa[MT][2];
@@ -180,14 +195,10 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
     v8i kb[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int r = 32 * kt + nn;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        // 16-byte chunks of the row this lane feeds (see mx_operand for MX)
-        const int j0 = MX ? 4 * st + hh : 4 * hh + 2 * st;
-        const int j1 = MX ? 4 * st + 2 + hh : 4 * hh + 2 * st + 1;
-        const uint4 lo = *(const uint4*)&kl[cur][kswz(r, j0)];
-        const uint4 hi = *(const uint4*)&kl[cur][kswz(r, j1)];
+        const uint4 lo = *(const uint4*)&kl[cur][kbase[st][0] + 4096 * kt];
+        const uint4 hi = *(const uint4*)&kl[cur][kbase[st][1] + 4096 * kt];
         kb[kt][st] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
@@ -224,10 +235,13 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
     const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
     float score = __uint_as_float(hv[0]) + __uint_as_float(hv[1]);
     if constexpr (!MX) score *= ks;
-    if (c * 64 + 63 > pos) score = c * 64 + lane > pos ? -INFINITY : score;
-    // the row's buffer ends at max_visible: the range check on the vector
-    // offset drops stores past it
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), srs, (c * 64 + lane) * 4, 0, 0);
+    const int lim = pos - 64 * c;  // keys of this page up to offset lim are visible
+    if (lim < 63) score = lane > lim ? -INFINITY : score;
+    // a descriptor over the row from this page on, ending at max_visible: its
+    // range check drops the stores past the row's end
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(srow + 64 * c, 0, (a.s.max_visible - 64 * c) * 4, kRawBuffer);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), prs, lane * 4, 0, 0);
   };
 
   for (int i = 0; i < nq; ++i) {
@@ -260,16 +274,18 @@ __global__ __launch_bounds__(kSThreads, 3) void k_index_scores_fp8_shared(IndexA
 #pragma unroll
       for (int k = 1; k < NPG; ++k) sel = (o >> 6) == k ? pg[k] : sel;
       const int page = __builtin_amdgcn_readlane(sel, o & 63);
-      const uint8_t* src = kpool + (int64_t)page * (kPage * 128) + sr * 128 + 16 * sj;
+      const __amdgpu_buffer_rsrc_t krs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kpool + (int64_t)page * (kPage * 128)), 0, kPage * 128, kRawBuffer);
+      // every wave loads the scales, wave 0 stores them: fp8 the key scale,
+      // MX the key's four group-scale bytes (as raw bits)
+      const void* sbase = MX ? (const void*)(a.k_mx + (int64_t)page * kPage * 4) : (const void*)(a.k_scale + (int64_t)page * kPage);
+      const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, kPage * 4, kRawBuffer);
       KStage g;
-      g.x = *(const uint4*)src;
-      g.y = *(const uint4*)(src + 16);
-      // every wave loads it, wave 0 stores it: fp8 the key scale, MX the key's
-      // four group-scale bytes (as raw bits)
-      if constexpr (MX)
-        g.s = __uint_as_float(*(const uint32_t*)(a.k_mx + ((int64_t)page * kPage + lane) * 4));
-      else
-        g.s = a.k_scale[(int64_t)page * kPage + lane];
+      const v4i x = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(krs, kvoff, 0, 0));
+      const v4i y = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(krs, kvoff + 16, 0, 0));
+      g.x = make_uint4(x[0], x[1], x[2], x[3]);
+      g.y = make_uint4(y[0], y[1], y[2], y[3]);
+      g.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksr, lane * 4, 0, 0));
       return g;
     };
     auto lwrite = [&](int buf, const KStage& g) __attribute__((always_inline)) {
