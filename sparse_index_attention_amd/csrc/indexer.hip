@@ -101,7 +101,6 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
 // ---------------------------------------------------------------------------
 constexpr int kSQ = 4;
 constexpr int kSChunk = 128;
-constexpr int kRawBuffer = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
 constexpr int kSThreads = 64 * kSQ;
 
 // Byte offset of 16-byte chunk j (0..7) of key row r in an LDS page: chunk j

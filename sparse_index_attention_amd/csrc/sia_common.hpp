@@ -15,6 +15,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 constexpr int kPage = 64;
+// buffer descriptor word 3: raw 32-bit data, range-checked (loads past the
+// range return zeros without touching memory, stores past it are dropped)
+constexpr int kRawBuffer = 0x00020000;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

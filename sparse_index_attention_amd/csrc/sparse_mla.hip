@@ -128,7 +128,6 @@ __global__ __launch_bounds__(256) void k_sparse_mla_f32(MlaArgs a) {
 constexpr int kDc = 512, kDr = 64, kD = kDc + kDr;
 constexpr int kChunks = kD / 8;                   // 72 chunks of 8 bf16 (16 bytes) per row
 constexpr int kRowsTile = 32;
-constexpr int kRawBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, range-checked
 // read for latent rows without a valid index when the pool is addressed directly
 __device__ uint4 g_zero_kv_row[kD * 2 / 16];
 constexpr int kTileBytes = kRowsTile * kD * 2;   // 36864
@@ -242,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   // descriptor's range, or a zero row), so that whatever the pool holds in
   // the row they would otherwise read, they contribute exactly nothing.
   const uint32_t kv_bytes = (uint32_t)((uint64_t)a.s.num_pages * kPage * (kD * 2));  // BUF only
-  const __amdgpu_buffer_rsrc_t kvrs = __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)kv_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t kvrs = __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)kv_bytes, kRawBuffer);
   // source of lane's 16-byte piece of chunk group 0 of tile row r: a buffer
   // offset (BUF) or an address
   auto row_src = [&](int slot, int r) __attribute__((always_inline)) -> uint64_t {
