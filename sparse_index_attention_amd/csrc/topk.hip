@@ -45,6 +45,7 @@ constexpr int kMaxBin = 256;
 constexpr int kBuf = kMaxK + kMaxBin;
 constexpr int kStreamWords = 8192;  // order-1 bitmap of streamed rows: 262144 positions
 constexpr int kDirect = 4096;
+constexpr int kStreamLoads = 8;     // loads in flight per thread in a streamed pass
 
 // ---- exact path ----------------------------------------------------------------
 struct ExactSmem {
@@ -210,32 +211,48 @@ union TopkSmem {
   ExactSmem x;
 };
 
+// threadIdx.x through an opaque move: positions derived from it are then
+// recomputed in each pass over the keys instead of being kept in sixty-four
+// registers across the passes.
+__device__ __forceinline__ int opaque_tid() {
+  int x;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(x) : "v"((int)threadIdx.x));
+  return x;
+}
+
 // Calls f(key, position) for every position of the row this thread covers;
 // key 0 marks a position past the row's end.  Position of register slot
-// (j, q): (j * kNT + tid) * 4 + q.
+// (j, q): (j * kNT + tid) * 4 + q (streamed rows: the same with j counting
+// the groups of four from the row's start).
 template <int PER, typename F>
 __device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1], const float* __restrict__ row,
                                          int n, F&& f) {
   if constexpr (PER > 0) {
+    const int tid = opaque_tid();
 #pragma unroll
     for (int j = 0; j < PER / 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) f(key[4 * j + q], (j * kNT + (int)threadIdx.x) * 4 + q);
+      for (int q = 0; q < 4; ++q) f(key[4 * j + q], (j * kNT + tid) * 4 + q);
   } else {
-    for (int i = (int)threadIdx.x * 4; i < n; i += kNT * 4) {
-      uint32_t k[4];
-      if (i + 4 <= n) {
-        const float4 v = *reinterpret_cast<const float4*>(row + i);
-        k[0] = f2key(v.x);
-        k[1] = f2key(v.y);
-        k[2] = f2key(v.z);
-        k[3] = f2key(v.w);
-      } else {
+    // streamed: kStreamLoads loads of four keys per thread are issued together
+    // (one memory latency per 32 768 keys, not per 4 096); the descriptor's
+    // range ends at the last whole group of four holding a visible key, and
+    // loads past it return zeros without a memory access
+    const __amdgpu_buffer_rsrc_t rrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, ((n + 3) & ~3) * 4, kRawBuffer);
+    const int tid = opaque_tid();
+    for (int base = 0; base < n; base += kNT * 4 * kStreamLoads) {
+      v4i v[kStreamLoads];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) k[q] = i + q < n ? f2key(row[i + q]) : 0u;
-      }
+      for (int u = 0; u < kStreamLoads; ++u)
+        v[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rrs, tid * 16, (base + u * kNT * 4) * 4, 0));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) f(k[q], i + q);
+      for (int u = 0; u < kStreamLoads; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int p = base + (u * kNT + tid) * 4 + q;
+          f(f2key(__int_as_float(v[u][q])) & (uint32_t)((p - n) >> 31), p);
+        }
     }
   }
 }
@@ -293,37 +310,32 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   // ---- 1. keys, range, sample ----------------------------------------------------
   uint32_t key[PER > 0 ? PER : 1];
   if constexpr (PER > 0) {
-    if constexpr (PER <= 32) {
-      // every load is unconditional, so that they are all in flight together
-      // instead of one branch, and one memory latency, at a time; a group past
-      // the visible keys re-reads the row's first four floats (a cache hit)
-      // rather than fetching keys it would mask.  Masks rather than selects: a
-      // select lets the compiler move a load under a branch and wait there.
+    // Every load is unconditional, so that a batch is in flight together
+    // instead of one branch, and one memory latency, per group of four.  The
+    // row goes through a buffer descriptor whose range ends at the last whole
+    // group of four holding a visible key (ld is a multiple of 4, so that
+    // group is inside the row): loads of later groups return zeros without a
+    // memory access, and each load needs only the lane's base offset plus a
+    // scalar one.  Keys past n are masked to 0.
+    const __amdgpu_buffer_rsrc_t rrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, ((n + 3) & ~3) * 4, kRawBuffer);
+    const int ltid = opaque_tid();
+    // eight loads in flight per thread at a time: all sixteen of the 64-key
+    // form would not fit the registers of sixteen waves
+    constexpr int kBatch = PER / 4 < kStreamLoads ? PER / 4 : kStreamLoads;
+    static_assert((PER / 4) % kBatch == 0, "whole batches of loads");
 #pragma unroll
-      for (int j = 0; j < PER / 4; ++j) {
-        const int i = (j * kNT + tid) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(row + (i < n && i + 4 <= ld ? i : 0));
-        key[4 * j] = f2key(v.x) & (0u - (uint32_t)(i < n));
-        key[4 * j + 1] = f2key(v.y) & (0u - (uint32_t)(i + 1 < n));
-        key[4 * j + 2] = f2key(v.z) & (0u - (uint32_t)(i + 2 < n));
-        key[4 * j + 3] = f2key(v.w) & (0u - (uint32_t)(i + 3 < n));
-      }
-    } else {
-      // 64 keys per thread: loading them all at once would not fit the
-      // registers of 16 waves, so the loads stay per group
+    for (int j0 = 0; j0 < PER / 4; j0 += kBatch) {
+      v4i v[kBatch];
 #pragma unroll
-      for (int j = 0; j < PER / 4; ++j) {
-        const int i = (j * kNT + tid) * 4;
-        if (i + 4 <= n) {
-          const float4 v = *reinterpret_cast<const float4*>(row + i);
-          key[4 * j] = f2key(v.x);
-          key[4 * j + 1] = f2key(v.y);
-          key[4 * j + 2] = f2key(v.z);
-          key[4 * j + 3] = f2key(v.w);
-        } else {
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rrs, ltid * 16, (j0 + u) * kNT * 16, 0));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) key[4 * j + q] = i + q < n ? f2key(row[i + q]) : 0u;
-        }
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + u, i = (j * kNT + ltid) * 4;
+        // all-ones for positions below n, from the sign of (position - n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = f2key(__int_as_float(v[u][q])) & (uint32_t)((i + q - n) >> 31);
       }
     }
   } else {
