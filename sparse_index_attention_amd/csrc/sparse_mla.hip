@@ -197,8 +197,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char tile2[kTileBytes];
-  __shared__ __attribute__((aligned(16))) int32_t sslot[kMaxSplitRows + 2 * kRowsTile];
-  __shared__ __attribute__((aligned(16))) float smask[kMaxSplitRows + 2 * kRowsTile];  // 0 or -inf per row
+  // slot table: the split's rows, two padding tiles, rounded up to whole
+  // rounds of the workgroup so that every thread writes every round (no
+  // branch for the compiler to sink the table loads into)
+  constexpr int RMAX = (kMaxSplitRows + 2 * kRowsTile + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) int32_t sslot[RMAX * NT];
+  __shared__ __attribute__((aligned(16))) float smask[RMAX * NT];  // 0 or -inf per row
   __shared__ __attribute__((aligned(16))) float4 xbuf[2 * NW * 4 * 64];   // partial S^T exchange, two parities
 
   // block -> (token, split, head part); blocks b and b + 8 share (token, split)
@@ -322,19 +326,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     }
   };
 
-  // ---- query operand: Q^T[depth, head], lane (hh, nn): head nn.  The wave's
-  // step j is global step st = 4(j/2) + 2ch + j%2, i.e. 16-byte chunk 2st + hh.
   v8bf qb[kHalfSteps];
+  // physical slots of all rows of this split (-1: no row).  The index loads go
+  // out first, then the query loads, then the page-table loads: loads complete
+  // in order, so the page-table loads wait only for the indices, and the
+  // query's 72 KB arrive while the table is resolved.
   {
-    const v8bf* qr = (const v8bf*)((const uint16_t*)a.q + ((int64_t)t * a.H + head) * kD);
-#pragma unroll
-    for (int j = 0; j < kHalfSteps; ++j) qb[j] = qr[2 * (4 * (j >> 1) + 2 * ch + (j & 1)) + hh];
-  }
-  // physical slots of all rows of this split (-1: no row), resolved once while
-  // the query loads are in flight: every index load is issued, then every
-  // page-table load, so the split pays two memory latencies, not two per row
-  {
-    constexpr int RMAX = (kMaxSplitRows + 2 * kRowsTile + NT - 1) / NT;
     const int rows = (ntiles + 2) * kRowsTile;
     // loads are unconditional (clamped indices) so that none waits for another
     int pos[RMAX];
@@ -343,6 +340,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const int j = j0 + tid + NT * u;
       pos[u] = irow[j < a.K ? j : a.K - 1];
     }
+    // query operand: Q^T[depth, head], lane (hh, nn): head nn.  The wave's
+    // step j is global step st = 4(j/2) + 2ch + j%2, i.e. 16-byte chunk 2st + hh.
+    const v8bf* qr = (const v8bf*)((const uint16_t*)a.q + ((int64_t)t * a.H + head) * kD);
+#pragma unroll
+    for (int j = 0; j < kHalfSteps; ++j) qb[j] = qr[2 * (4 * (j >> 1) + 2 * ch + (j & 1)) + hh];
     int page[RMAX];
 #pragma unroll
     for (int u = 0; u < RMAX; ++u) {
@@ -354,8 +356,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const int r = tid + NT * u, p = pos[u];
       const bool ok = r < rows && j0 + r < j1 && p >= 0 && p < a.s.max_visible;
       const int pg = clampi(page[u], 0, a.s.num_pages - 1);
-      if (r < rows) sslot[r] = ok ? pg * kPage + (p & (kPage - 1)) : -1;
-      if (r < rows) smask[r] = ok ? 0.f : -INFINITY;
+      sslot[r] = ok ? pg * kPage + (p & (kPage - 1)) : -1;
+      smask[r] = ok ? 0.f : -INFINITY;
     }
   }
   // keep the query operand resident: without this the compiler re-loads it
