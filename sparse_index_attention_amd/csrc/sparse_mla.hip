@@ -404,8 +404,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   // ---- software-pipelined tiles ------------------------------------
   // Iteration i requests tile i+2 into the buffer tile i-1 used, computes the
   // partial scores of tile i+1 while the softmax of tile i runs between its
-  // MFMAs, then O += V^T P^T for tile i, and ends with the one barrier that
-  // publishes tile i+2 and the partial scores of tile i+1.  bf16 rows go
+  // MFMAs (starting with the read of the partner's half of tile i), then
+  // O += V^T P^T for tile i, writes its half of tile i+1, and ends with the
+  // one barrier that publishes tile i+2 and the partial scores of tile i+1.  bf16 rows go
   // straight into LDS; fp8 rows are loaded into registers at the start of the
   // iteration and dequantized into the buffer after the output MFMAs.
   // Requests and score passes past the last tile run on the slot table's -1
@@ -448,19 +449,24 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) mine[64 * k] = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
   };
-  // both waves of a head block add the same two fp32 values: identical S^T
-  auto xadd = [&](v16f& acc, int par) __attribute__((always_inline)) {
+  // both waves of a head block add the same two fp32 values: identical S^T.
+  // The partner's half is read as the next iteration's score MFMAs start, so
+  // the read's latency runs beside them.
+  auto xload = [&](float4 (&xo)[4], int par) __attribute__((always_inline)) {
     const float4* other = xbuf + (par * NW + partner) * 256 + lane;
 #pragma unroll
+    for (int k = 0; k < 4; ++k) xo[k] = other[64 * k];
+  };
+  auto xadd = [&](v16f& acc, const float4 (&xo)[4]) __attribute__((always_inline)) {
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 v = other[64 * k];
-      acc[4 * k] += v.x;
-      acc[4 * k + 1] += v.y;
-      acc[4 * k + 2] += v.z;
-      acc[4 * k + 3] += v.w;
+      acc[4 * k] += xo[k].x;
+      acc[4 * k + 1] += xo[k].y;
+      acc[4 * k + 2] += xo[k].z;
+      acc[4 * k + 3] += xo[k].w;
     }
   };
-  v16f sacc;   // full S^T of the tile the next iteration finishes
+  v16f sacc;   // this wave's half of S^T of the tile the next iteration finishes
   // gather of tile i+2: source rows first, then every 16-byte request right
   // after the first score MFMA (issued together, they land earlier than when
   // spread over the score steps)
@@ -488,6 +494,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     float sv[16];
     float tloc = -INFINITY, psum = 0.f, mneg = 0.f;
     v8bf pb[2];
+    float4 xo[4];
     auto soft = [&](int j) __attribute__((always_inline)) {
       if constexpr (!FP8) {
         if (j == 0) {
@@ -496,13 +503,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         }
       }
       if (j == 0) {
+        xload(xo, i & 1);   // the partner's half of tile i, published by the last barrier
+      } else if (j == 2) {
+        xadd(sacc, xo);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float4 f = fl.f[r >> 2];
           sv[r] = sacc[r] + ((r & 3) == 0 ? f.x : (r & 3) == 1 ? f.y : (r & 3) == 2 ? f.z : f.w);
           tloc = fmaxf(tloc, sv[r]);
         }
-      } else if (j == 1) {
+      } else if (j == 3) {
         tloc *= a.scale_log2;  // the scale is positive
         m_seen = fmaxf(m_seen, tloc);
         if (__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
@@ -512,10 +522,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         }
         overflow |= tloc > m_ref + 100.f;
         mneg = m_ref == -INFINITY ? -INFINITY : -m_ref;   // no valid row yet: every p is 0
-      } else if (j < 10) {
+      } else if (j >= 4 && j < 12) {
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
-          const int r = 2 * (j - 2) + rr;
+          const int r = 2 * (j - 4) + rr;
           const float pv = fast_exp2(fmaf(sv[r], a.scale_log2, mneg));
           psum += pv;
           pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
@@ -523,7 +533,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       }
     };
     v16f snext = s_partial(nxt, soft);
-    xwrite(snext, (i + 1) & 1);
     // O^T += V^T . P^T for tile i; MFMA mf covers tile rows 16mf + R(hh, jj)
     auto vfrag = [&](int vt, int mf) -> v8bf {
       const int imm = 4096 * (vt >> 1) + 2048 * mf;
@@ -541,12 +550,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       if (k + PFV < 2 * kVT) vring[k % PFV] = vfrag((k + PFV) % kVT, (k + PFV) / kVT);
       o[vt] = mfma_bf16(af, pb[mf], o[vt]);
     }
+    // the partial scores of tile i+1 go out after the output MFMAs are issued:
+    // by then the score chain has finished, so the writes do not wait for it
+    xwrite(snext, (i + 1) & 1);
     if constexpr (FP8) commit_fp8(fut);  // tile i+2: buffer free since the last barrier
     l_run += psum;
     // tile i+2 is in LDS and the partial scores of tile i+1 are published
     wait_vm_lgkm0<0>();
     asm volatile("s_barrier" ::: "memory");
-    xadd(snext, (i + 1) & 1);
     sacc = snext;
   };
   for (int pass = 0; pass < 2; ++pass) {
@@ -570,11 +581,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     }
     wait_vm_lgkm0<0>();
     asm volatile("s_barrier" ::: "memory");
+    // this wave's half of the scores of tile 0; iteration 0 adds the partner's
     sacc = s_partial(T0, [](int) {});
     xwrite(sacc, 0);
     wait_vm_lgkm0<63>();
     asm volatile("s_barrier" ::: "memory");
-    xadd(sacc, 0);
     int i = 0;
     for (; i + 3 <= ntiles; i += 3) {
       iter(i, T0, T1, T2);
