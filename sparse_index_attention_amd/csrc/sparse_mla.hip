@@ -43,7 +43,8 @@ struct MlaArgs {
   const void* q;
   const void* kv;
   const float* kv_scale;
-  int scale_tokens, scale_elems;  // fp8 tiles
+  int scale_tokens, scale_elems;  // fp8 tiles (powers of two)
+  int log2_scale_tokens, log2_scale_elems;
   int H;
   int Dc, Dr;
   SeqArgs s;
@@ -281,21 +282,42 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   v4i stage[FP8 ? kFp8Loads : 1];
   float stage_scale[FP8 ? kFp8Loads : 1];
   const int f_row = tid / TPR, f_sub = tid % TPR;
+  // fp8 pool and scales below 4 GiB (BUF): buffer descriptors, so that a row
+  // without an index reads zeros from an offset past the range (no select, no
+  // 64-bit address arithmetic per load)
+  const uint32_t kv8_bytes = (uint32_t)((uint64_t)a.s.num_pages * kPage * 640);  // FP8 && BUF only
+  const uint32_t sc_bytes = (uint32_t)(((uint64_t)a.s.num_pages * kPage * kDc >> (a.log2_scale_tokens + a.log2_scale_elems)) * 4);
+  const __amdgpu_buffer_rsrc_t kv8rs = __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)kv8_bytes, kRawBuffer);
+  const __amdgpu_buffer_rsrc_t scrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.kv_scale, 0, (int)sc_bytes, kRawBuffer);
   auto issue_fp8 = [&](int i) __attribute__((always_inline)) {
     const int32_t* ss = sslot + i * kRowsTile;
     const bool valid = ss[f_row] >= 0;  // otherwise zeros, whatever slot 0 holds
     const int slot = valid ? ss[f_row] : 0;
-    const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
+    // scale tile sizes are powers of two: shifts, not divisions, on the gather path
     const int page = slot >> 6, tok = slot & 63;
-    const int tiles_tok = kPage / a.scale_tokens, tiles_el = kDc / a.scale_elems;
-    const int64_t sbase = ((int64_t)page * tiles_tok + tok / a.scale_tokens) * tiles_el;
+    const int lt = a.log2_scale_tokens, le = a.log2_scale_elems;
+    const int64_t sbase = (((int64_t)page << (6 - lt)) + (tok >> lt)) << (9 - le);
+    if constexpr (BUF) {
+      const uint32_t row_off = valid ? (uint32_t)slot * 640u + 16u * f_sub : kv8_bytes;
+      const uint32_t sc_off = valid ? (uint32_t)sbase * 4u : sc_bytes;
 #pragma unroll
-    for (int m = 0; m < kFp8Loads; ++m) {
-      const int c = f_sub + TPR * m;
-      const v4i v = *(const v4i*)(src + 16 * TPR * m);
-      stage[m] = valid ? v : v4i{0, 0, 0, 0};
-      const float sc = c < 32 ? a.kv_scale[sbase + (16 * c) / a.scale_elems] : 1.f;
-      stage_scale[m] = valid ? sc : 0.f;
+      for (int m = 0; m < kFp8Loads; ++m) {
+        const int c = f_sub + TPR * m;
+        stage[m] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kv8rs, row_off, 16 * TPR * m, 0));
+        // latent chunks take their tile's scale, the rope chunks 1 (0 for a row without an index)
+        const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, sc_off + 4u * ((16u * c) >> le), 0, 0));
+        stage_scale[m] = c < 32 ? sc : (valid ? 1.f : 0.f);
+      }
+    } else {
+      const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
+#pragma unroll
+      for (int m = 0; m < kFp8Loads; ++m) {
+        const int c = f_sub + TPR * m;
+        const v4i v = *(const v4i*)(src + 16 * TPR * m);
+        stage[m] = valid ? v : v4i{0, 0, 0, 0};
+        const float sc = c < 32 ? a.kv_scale[sbase + ((16 * c) >> le)] : 1.f;
+        stage_scale[m] = valid ? sc : 0.f;
+      }
     }
   };
   auto commit_fp8 = [&](lds_u8* dst) __attribute__((always_inline)) {
@@ -729,6 +751,8 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
   a.kv_scale = kv.kv_scale;
   a.scale_tokens = kv.scale_tokens;
   a.scale_elems = kv.scale_elems;
+  a.log2_scale_tokens = __builtin_ctz((unsigned)(kv.scale_tokens > 0 ? kv.scale_tokens : 1));
+  a.log2_scale_elems = __builtin_ctz((unsigned)(kv.scale_elems > 0 ? kv.scale_elems : 1));
   a.H = heads;
   a.Dc = kv.latent_dim;
   a.Dr = kv.rope_dim;
@@ -761,8 +785,13 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
   // bf16 pools that buffer offsets (32 bits) can address take the buffer form
   // (with room past the end for the zero-row offsets)
   const bool buf = (uint64_t)s.num_pages * kPage * (kD * 2) <= 0xfffff000ull;
+  // fp8 rows are 640 bytes; the scale array must fit a descriptor too
+  const uint64_t sc_entries = ((uint64_t)s.num_pages * kPage * kDc) >> (a.log2_scale_tokens + a.log2_scale_elems);
+  const bool buf8 = (uint64_t)s.num_pages * kPage * 640 <= 0xfffff000ull && sc_entries * 4 <= 0xfffff000ull;
 #define SIA_LAUNCH_MLA(NW)                                                                   \
-  if (fp8)                                                                                   \
+  if (fp8 && buf8)                                                                           \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, true>), grid, dim3(NW * 64), 0, st, a);  \
+  else if (fp8)                                                                              \
     hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, false>), grid, dim3(NW * 64), 0, st, a); \
   else if (buf)                                                                              \
     hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false, true>), grid, dim3(NW * 64), 0, st, a); \

@@ -312,6 +312,41 @@ def test_sparse_mla_pool_beyond_4gib():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["quant_decode_tiny", "quant_decode_tile128_tiny"])
+def test_sparse_mla_fp8_pool_beyond_4gib(name):
+    """fp8 latent pools (640-byte rows) under 4 GiB are gathered through
+    buffer descriptors, larger ones through 64-bit addresses.  The same pages
+    and scales placed at the top of a 4.4 GB pool (every other page and scale
+    NaN) give bit-identical outputs, and both match the oracle."""
+    wl = workload(name)
+    K, H = wl.cfg["K"], wl.cfg["H"]
+    seq, _, q, kv = upload(wl)
+    _, sel, att = oracle_run(name)
+    idx = dev(np.stack([sel[t] for t in range(wl.Tq)]).astype(np.int32))
+    P = kv.pool.shape[0]
+    big_pages = 105000   # 105000 x 64 rows x 640 bytes = 4.30 GB
+    assert big_pages * 64 * 640 > 2**32 and P < big_pages
+    base = big_pages - P
+    print(f"[mla-big-pool-fp8] {name}: {P} pages placed at {base}..{big_pages - 1}", flush=True)
+    big = torch.full((big_pages,) + tuple(kv.pool.shape[1:]), 0xFF, dtype=torch.uint8, device="cuda")  # NaN codes
+    big[base:].copy_(kv.pool)
+    sbig = torch.full((big_pages,) + tuple(kv.scale.shape[1:]), float("nan"), dtype=torch.float32, device="cuda")
+    sbig[base:].copy_(kv.scale)
+    kv_big = sia.LatentKV(big, 512, 64, sbig, kv.scale_tokens, kv.scale_elems)
+    seq_big = sia.SeqMap(seq.q_seq, seq.q_pos, seq.block_table + base, big_pages, wl.max_visible)
+    for fn in (sia.sparse_mla_decode, sia.sparse_mla_prefill):
+        la = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+        lb = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+        a = fn(q, kv, seq, idx, K, wl.softmax_scale, lse=la)
+        b = fn(q, kv_big, seq_big, idx, K, wl.softmax_scale, lse=lb)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), fn.__name__
+        assert torch.equal(la, lb), fn.__name__
+        check_attention("fp8", to_np_out(b), lb.cpu().numpy(), att, range(wl.Tq))
+    del big, sbig
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["decode_tiny", "quant_decode_tiny", "prefill_tiny"])
 def test_sparse_mla_padding_rows_ignore_pool_contents(name):
     """Index lists padded with -1 (and holes) must not depend on what the pool
