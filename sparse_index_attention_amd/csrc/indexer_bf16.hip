@@ -23,7 +23,6 @@ constexpr int kBQ = 4;                 // queries (waves) per workgroup
 constexpr int kBThreads = 64 * kBQ;
 constexpr int kBMaxChunk = 128;        // pages per work item, at most
 constexpr int kBRow = 256;             // bytes of a bf16 key row
-constexpr int kBRawBuffer = 0x00020000;
 
 // 16-byte chunk j (0..15) of key row r sits at chunk j ^ (r & 15): the 16 lanes
 // of one read phase (rows r..r+15, same j) cover all 64 banks.
@@ -66,7 +65,7 @@ __global__ __launch_bounds__(kBThreads, 2) void k_index_scores_bf16(IndexArgs a,
   const int my_seq = has_q ? clampi(a.s.q_seq[t], 0, a.s.batch - 1) : -1;
   const int c_own = (pos >> 6) + 1;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      a.scores + (int64_t)(has_q ? t : 0) * a.ld, 0, a.s.max_visible * 4, kBRawBuffer);
+      a.scores + (int64_t)(has_q ? t : 0) * a.ld, 0, a.s.max_visible * 4, kRawBuffer);
   const uint8_t* __restrict__ kpool = (const uint8_t*)a.k_pool;
   const int sr = tid >> 2, sj = 4 * (tid & 3);  // thread moves row sr, chunks sj .. sj+3
 
