@@ -220,10 +220,10 @@ __device__ __forceinline__ int opaque_tid() {
   return x;
 }
 
-// Calls f(key, position) for every position of the row this thread covers;
-// key 0 marks a position past the row's end.  Position of register slot
-// (j, q): (j * kNT + tid) * 4 + q (streamed rows: the same with j counting
-// the groups of four from the row's start).
+// Calls f(key, position, slot) for every position of the row this thread
+// covers; key 0 marks a position past the row's end.  Position of register
+// slot 4j + q: (j * kNT + tid) * 4 + q (streamed rows: the same with j
+// counting the groups of four from the row's start, and slot -1).
 template <int PER, typename F>
 __device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1], const float* __restrict__ row,
                                          int n, F&& f) {
@@ -232,7 +232,7 @@ __device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1
 #pragma unroll
     for (int j = 0; j < PER / 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) f(key[4 * j + q], (j * kNT + tid) * 4 + q);
+      for (int q = 0; q < 4; ++q) f(key[4 * j + q], (j * kNT + tid) * 4 + q, 4 * j + q);
   } else {
     // streamed: kStreamLoads loads of four keys per thread are issued together
     // (one memory latency per 32 768 keys, not per 4 096); the descriptor's
@@ -251,18 +251,21 @@ __device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int p = base + (u * kNT + tid) * 4 + q;
-          f(f2key(__int_as_float(v[u][q])) & (uint32_t)((p - n) >> 31), p);
+          f(f2key(__int_as_float(v[u][q])) & (uint32_t)((p - n) >> 31), p, -1);
         }
     }
   }
 }
 
 // PER keys per thread live in registers (rows up to kNT * PER); PER = 0 streams
-// the row from memory on every pass.
-template <int PER>
+// the row from memory on every pass.  CAND: the rows are candidate lists with a
+// map back to positions; with PER <= 32 each thread also holds the positions
+// of its keys, so that score-order output needs no dependent load of the map.
+template <int PER, bool CAND>
 __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, int64_t ld, SeqArgs s, int K,
                                               int order, int32_t* __restrict__ idx, float* __restrict__ vals,
                                               CandMap cm) {
+  constexpr bool kCarry = CAND && PER > 0 && PER <= 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   TopkSmem<PER>& smem = *reinterpret_cast<TopkSmem<PER>*>(smem_raw);
   FastSmem<PER>& sh = smem.f;
@@ -341,8 +344,21 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   } else {
     key[0] = 0u;
   }
+  // positions of this thread's candidates (same slots as the keys)
+  int cpos[kCarry ? PER : 1];
+  if constexpr (kCarry) {
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)pmap, 0, ((n + 3) & ~3) * 4, kRawBuffer);
+    const int ltid = opaque_tid();
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(prs, ltid * 16, j * kNT * 16, 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cpos[4 * j + q] = v[q];
+    }
+  }
   uint32_t kmn = 0xffffffffu, kmx = 0u;
-  for_keys<PER>(key, row, n, [&](uint32_t k, int) {
+  for_keys<PER>(key, row, n, [&](uint32_t k, int, int) {
     kmn = min(kmn, k ? k : 0xffffffffu);
     kmx = max(kmx, k);
   });
@@ -397,7 +413,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
 
   // ---- 2. histogram of the keys >= L ---------------------------------------------
   const int sh2 = bin_shift((uint64_t)kmax - L + 1);
-  for_keys<PER>(key, row, n, [&](uint32_t k, int) {
+  for_keys<PER>(key, row, n, [&](uint32_t k, int, int) {
     if (k >= L) atomicAdd(&sh.hist[(k - L) >> sh2], 1u);
   });
   __syncthreads();
@@ -434,10 +450,14 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   }
 
   // ---- 3. scatter bins >= b*, rank inside each bin ---------------------------------
-  for_keys<PER>(key, row, n, [&](uint32_t k, int p) {
+  for_keys<PER>(key, row, n, [&](uint32_t k, int p, int slot) {
     if (k >= L) {
       const uint32_t b = (k - L) >> sh2;
-      if (b >= bstar) sh.buf[sh.above[b] + atomicAdd(&sh.cur[b], 1u)] = composite(k, p);
+      // carrying positions, the composite holds the key's position itself
+      // (candidates are in position order, so the order of ties is unchanged)
+      int tag = p;
+      if constexpr (kCarry) tag = order == 0 ? cpos[slot < 0 ? 0 : slot] : p;
+      if (b >= bstar) sh.buf[sh.above[b] + atomicAdd(&sh.cur[b], 1u)] = composite(k, tag);
     }
   });
   __syncthreads();
@@ -452,7 +472,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
     if (fin < usel) {
       const int p = (int)(uint32_t)v;
       if (order == 0) {
-        orow[fin] = pmap ? pmap[p] : p;
+        orow[fin] = (pmap && !kCarry) ? pmap[p] : p;
         if (vrow) vrow[fin] = key2f(k);
       } else {
         atomicOr(&sh.bitmap[p >> 5], 1u << (p & 31));
@@ -484,14 +504,21 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
   }
 }
 
+template <int PER, bool CAND>
+static hipError_t launch_rows_as(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
+                                 float* vals, const CandMap& cm, hipStream_t st) {
+  const size_t shm = sizeof(TopkSmem<PER>);
+  hipError_t e =
+      hipFuncSetAttribute((const void*)k_topk<PER, CAND>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_topk<PER, CAND>), dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals, cm);
+  return hipGetLastError();
+}
 template <int PER>
 static hipError_t launch_rows(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
                               float* vals, const CandMap& cm, hipStream_t st) {
-  const size_t shm = sizeof(TopkSmem<PER>);
-  hipError_t e = hipFuncSetAttribute((const void*)k_topk<PER>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_topk<PER>, dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals, cm);
-  return hipGetLastError();
+  return cm.pos ? launch_rows_as<PER, true>(scores, ld, s, K, order, idx, vals, cm, st)
+                : launch_rows_as<PER, false>(scores, ld, s, K, order, idx, vals, cm, st);
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
