@@ -206,20 +206,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) float smask[RMAX * NT];  // 0 or -inf per row
   __shared__ __attribute__((aligned(16))) float4 xbuf[2 * NW * 4 * 64];   // partial S^T exchange, two parities
 
-  // block -> (token, split, head part); blocks b and b + 8 share (token, split)
+  // block -> (token, split, head part).  Workgroups are dispatched to the
+  // eight XCDs round-robin (block b on XCD b % 8), so every workgroup of token
+  // t is given a block on XCD t % 8: the head parts of a (token, split) share
+  // the gathered rows through that XCD's L2, and the splits of a token share
+  // its query rows.
   const int parts = a.H / (32 * HBW);
   const int bid = blockIdx.x;
-  const int grp = bid / (8 * parts), within = bid % (8 * parts);
-  const int part = within >> 3;
-  const int unit = grp * 8 + (within & 7);     // token * splits + split
-  if (unit >= a.s.T * a.splits) return;
+  const int slot = bid >> 3;                   // ((t / 8) * splits + split) * parts + part
+  const int part = slot % parts;
+  const int split = (slot / parts) % a.splits;
+  const int t = (slot / parts / a.splits) * 8 + (bid & 7);
+  if (t >= a.s.T) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, nn = lane & 31;
   const int hbl = wave % HBW, ch = wave / HBW;   // head block in the workgroup, column (and depth) half
   const int partner = (1 - ch) * HBW + hbl;
-  const int split = unit % a.splits;
-  const int t = unit / a.splits;
   const int j0 = split * a.rows_per_split;
   int j1 = j0 + a.rows_per_split;
   j1 = j1 < a.K ? j1 : a.K;
@@ -776,9 +779,9 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
     a.ws_o = (uint16_t*)ws;
     a.ws_lse = (float*)(a.ws_o + (size_t)s.T * a.splits * heads * kDc);
   }
-  const int64_t units = (int64_t)s.T * a.splits;
+  const int64_t units = ((int64_t)(s.T + 7) / 8) * a.splits;   // per XCD
   const int parts = heads >= 128 ? 2 : 1;
-  const int64_t nblocks = ((units + 7) / 8) * 8 * parts;
+  const int64_t nblocks = units * parts * 8;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nblocks);
   const bool fp8 = kv.dtype == SIA_FP8_E4M3;
