@@ -174,8 +174,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 16-deep steps, both write their partial S^T to LDS, and each adds the
 // other's.  Each wave therefore keeps only its half of the query operand in
 // registers (18 steps), and a tile costs a wave 18 + 16 MFMAs.  With 128 heads a
-// (token, split) takes two workgroups; blocks b and b + 8 are those two and are
-// scheduled on the same XCD, so the second gather of the rows is served by its L2.
+// (token, split) takes two workgroups.  All workgroups of a token run on one
+// XCD (see the block mapping), so the second gather of a row and the splits'
+// query loads are served by its L2.
 constexpr int kVH = 256;
 constexpr int kMaxSplitRows = 2048;      // rows of one split, slots resolved once per workgroup
 constexpr int kHalfSteps = 18;           // score steps per wave
