@@ -11,6 +11,9 @@
 
 namespace sia {
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), no wait on expcnt or lgkmcnt
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
 struct IndexArgs {
   const void* q;
   const float* q_scale;   // fp8: per token or per (token, head)
@@ -68,24 +71,26 @@ __device__ __forceinline__ v8i mx_operand(const uint8_t* row, int hh) {
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// One wave scores query t against 64-key pages of its sequence's block table
-// and calls sink(s, score) once per page with lane l holding key s = 64c + l
-// (scores of keys past pos are -inf).  The pages are c = claim(), claim(), ...
-// until claim() returns -1; claim() must return a wave-uniform value and, once
-// it has returned -1, keep doing so.
+// One wave scores query t against 64-key pages of its sequence and calls
+// sink(s, score) once per page with lane l holding key s = 64c + l (scores of
+// keys past pos are -inf).  The pages are c = claim(), claim(), ... until
+// claim() returns -1; claim() must return a wave-uniform value and, once it
+// has returned -1, keep doing so.  page_of(c) gives the physical page of
+// logical page c (wave-uniform).  It must not read global memory: a vector
+// memory load in the loop would make the wave wait for every page load in
+// flight before it (their counter drains in order), which empties the ring.
 // Lane l: nn = l % 32 (key within an N tile / head within an M tile), hh = l / 32.
 // K-step mapping (same for both operands): step st of lane half hh covers
 // depth bytes [64*hh + 32*st, 64*hh + 32*st + 32).
 // MX: MXFP8 inputs (group scales inside the MFMA; no per-token scales).
-template <int HI, bool MX, typename Claim, typename Sink>
-__device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, int pos, int b, Claim&& claim,
-                                                    Sink&& sink) {
+template <int HI, bool MX, typename Claim, typename PageOf, typename Sink>
+__device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, int pos, Claim&& claim,
+                                                    PageOf&& page_of, Sink&& sink) {
   constexpr int MT = HI / 32;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5, nn = lane & 31;
   const uint8_t* __restrict__ kpool = (const uint8_t*)a.k_pool;
   const uint8_t* __restrict__ qbase = (const uint8_t*)a.q;
-  const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
 
   // key pages go through a ring of three register buffers: while page c is
   // computed, pages c+1 and c+2 are in flight
@@ -95,27 +100,48 @@ __device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, i
     float f;
     uint32_t w[2];
   };
+  // Every page request is unconditional: the page goes through a buffer
+  // descriptor built in scalar registers, and for c < 0 (nothing left to
+  // claim) the descriptor's range is empty, so the loads return zeros without
+  // a memory access.  With conditional requests the compiler could not count
+  // the loads in flight and waited for all of them before each page's first
+  // MFMAs, which kept about one page in flight per wave instead of two.
   auto load_page = [&](int c, v8i (&kb)[2][2], KScale& ks) __attribute__((always_inline)) {
-    int page = table[c];
+    c = __builtin_amdgcn_readfirstlane(c);   // wave-uniform: the descriptors stay in scalar registers
+    int page = page_of(c);
     page = page < 0 ? 0 : (page >= a.s.num_pages ? a.s.num_pages - 1 : page);
+    page = __builtin_amdgcn_readfirstlane(page);
+    const bool ok = c >= 0;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kpool + (int64_t)page * (kPage * 128)), 0, ok ? kPage * 128 : 0, kRawBuffer);
+    auto ld16 = [&](int off) __attribute__((always_inline)) {
+      return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+    };
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint8_t* kr = kpool + (int64_t)page * (kPage * 128) + (32 * kt + nn) * 128;
-      if constexpr (MX) {
-        kb[kt][0] = mx_operand<0>(kr, hh);
-        kb[kt][1] = mx_operand<1>(kr, hh);
-      } else {
-        kb[kt][0] = *(const v8i*)(kr + 64 * hh);
-        kb[kt][1] = *(const v8i*)(kr + 64 * hh + 32);
+      const int row = (32 * kt + nn) * 128;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        // MX: depth [64x + 16hh, +16) and [64x + 32 + 16hh, +16) (see mx_operand);
+        // fp8: depth [64hh + 32x, +32)
+        const int o0 = MX ? row + 64 * x + 16 * hh : row + 64 * hh + 32 * x;
+        const int o1 = MX ? o0 + 32 : o0 + 16;
+        const v4i lo = ld16(o0), hi = ld16(o1);
+        kb[kt][x] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     }
+    const void* sbase = MX ? (const void*)(a.k_mx + (int64_t)page * kPage * 4) : (const void*)(a.k_scale + (int64_t)page * kPage);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)sbase, 0, ok ? kPage * 4 : 0, kRawBuffer);
     if constexpr (MX) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
-        ks.w[kt] = mx_lane_scales(*(const uint32_t*)(a.k_mx + ((int64_t)page * kPage + 32 * kt + nn) * 4), hh);
+        ks.w[kt] = mx_lane_scales(__builtin_amdgcn_raw_buffer_load_b32(srs, (32 * kt + nn) * 4, 0, 0), hh);
     } else {
-      ks.f = a.k_scale[(int64_t)page * kPage + lane];
+      ks.f = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, 0, 0));
     }
+    // keep the requests here: without this the compiler sinks them past the
+    // loop's exit test into the next step, one page later
+    asm volatile("" ::: "memory");
   };
   v8i k0[2][2], k1[2][2], k2[2][2];
   KScale ks0{}, ks1{}, ks2{};
@@ -123,9 +149,9 @@ __device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, i
   if (c0 < 0) return;
   load_page(c0, k0, ks0);
   int c1 = claim();
-  if (c1 >= 0) load_page(c1, k1, ks1);
+  load_page(c1, k1, ks1);
   int c2 = claim();
-  if (c2 >= 0) load_page(c2, k2, ks2);
+  load_page(c2, k2, ks2);
 
   // query operand (A): head m = 32*mt + nn
   v8i qa[MT][2];
@@ -150,9 +176,15 @@ __device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, i
       wr[mt][r] = a.w[(int64_t)t * HI + head] * qs;
     }
   }
+  // Everything loaded so far (the first three pages, the query and its
+  // weights) lands before the loop starts.  Otherwise the compiler's wait for
+  // the query operand, needed on the first pass only, stays at the loop head
+  // as a wait for every load in flight and runs on every pass.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   // scores of page c from buffer kb, then buffer kb takes the next claimed
   // page (returned; -1 when none is left)
   auto step = [&](int c, v8i (&kb)[2][2], KScale& ks) __attribute__((always_inline)) -> int {
+    if (c >= 0) {   // wave-uniform; the buffer's request below is unconditional
     float p[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -184,28 +216,40 @@ __device__ __forceinline__ void score_claimed_pages(const IndexArgs& a, int t, i
     const int s = c * 64 + lane;
     if (s > pos) score = -INFINITY;
     sink(s, score);
+    }
     const int next = claim();
-    if (next >= 0) load_page(next, kb, ks);
+    load_page(next, kb, ks);
     return next;
   };
-  // pages are claimed in processing order, so the first -1 ends the ring
+  // Pages are claimed in processing order, so once a round has claimed -1
+  // for buffer 0 the two later buffers hold -1 as well.  The one exit test
+  // per round keeps every path into the loop head the same: with an exit
+  // after each step the compiler merged the exits into a path that skipped
+  // two buffers' requests, and waited for every load in flight at the head.
   while (true) {
     c0 = step(c0, k0, ks0);
-    if (c1 < 0) break;
     c1 = step(c1, k1, ks1);
-    if (c2 < 0) break;
     c2 = step(c2, k2, ks2);
     if (c0 < 0) break;
   }
 }
 
-// The pages [c_begin, c_end) in order.
+// The pages [c_begin, c_end) in order, c_begin < c_end <= c_begin + 64.
+// Their physical pages are loaded once, one per lane (lane l: page
+// c_begin + l), and read with a lane select.
 template <int HI, bool MX, typename Sink>
 __device__ __forceinline__ void score_pages(const IndexArgs& a, int t, int pos, int b, int c_begin, int c_end,
                                             Sink&& sink) {
+  const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
+  const int lane = threadIdx.x & 63;
+  const int win = table[min(c_begin + lane, c_end - 1)];
   int next = c_begin;
-  score_claimed_pages<HI, MX>(a, t, pos, b, [&]() __attribute__((always_inline)) { return next < c_end ? next++ : -1; },
-                              sink);
+  score_claimed_pages<HI, MX>(
+      a, t, pos, [&]() __attribute__((always_inline)) { return next < c_end ? next++ : -1; },
+      [&](int c) __attribute__((always_inline)) {
+        return __builtin_amdgcn_readlane(win, __builtin_amdgcn_readfirstlane(max(c - c_begin, 0)));
+      },
+      sink);
 }
 
 }  // namespace sia

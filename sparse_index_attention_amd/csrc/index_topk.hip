@@ -45,6 +45,7 @@ struct RangeSmem {
   uint32_t scan[2][kRNW];
   uint32_t found_bin, found_above, found_cnt, list_n, found_key, found_need;
   uint32_t next_page;  // pages of the range claimed so far
+  int32_t pages[kRangePages];  // physical pages of the range
 };
 
 template <int HI, bool MX>
@@ -70,17 +71,40 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
   // ---- 1. scores of the range into LDS.  The waves claim pages one at a
   // time from a shared counter: with a fixed share each, the slowest wave's
   // memory latency would hold up the whole workgroup at the barrier.
-  if (tid == 0) sh.next_page = 0;
+  // The range's block-table entries go to LDS first, so that the page loop
+  // looks them up without a memory load.
+  // The first histogram pass's bins are cleared here as well, and each lane
+  // tracks the key range of the scores it writes, so that the selection
+  // starts right after the scoring barrier.
+  if (tid == 0) {
+    sh.next_page = 0;
+    sh.list_n = 0;
+  }
+  if (tid < kRangePages) sh.pages[tid] = a.s.block_table[(int64_t)b * a.s.max_pages + min(c0 + tid, c1 - 1)];
+  for (int i = tid; i < kRBins; i += kRNT) sh.hist[i] = 0;
+  uint32_t lmn = 0xffffffffu, lmx = 0u;
   __syncthreads();
   score_claimed_pages<HI, MX>(
-      a, t, pos, b,
+      a, t, pos,
       [&]() __attribute__((always_inline)) -> int {
         uint32_t v = 0;
         if (lane == 0) v = atomicAdd(&sh.next_page, 1u);
         const int c = c0 + __builtin_amdgcn_readfirstlane((int)v);
         return c < c1 ? c : -1;
       },
-      [&](int s, float score) __attribute__((always_inline)) { sh.sc[s - key0] = score; });
+      [&](int c) __attribute__((always_inline)) { return sh.pages[c < c0 ? 0 : c - c0]; },
+      [&](int s, float score) __attribute__((always_inline)) {
+        sh.sc[s - key0] = score;
+        const uint32_t k = s <= pos ? f2key(score) : 0u;  // 0: past the range's keys
+        lmn = k && k < lmn ? k : lmn;
+        lmx = k > lmx ? k : lmx;
+      });
+  lmn = wave_all(lmn, 0xffffffffu, OpMin{});
+  lmx = wave_all(lmx, 0u, OpMax{});
+  if (lane == 0) {
+    sh.red[0][w] = lmn;
+    sh.red[1][w] = lmx;
+  }
   __syncthreads();
 
   // ---- 2. keys in registers: thread tid holds positions 16*tid .. 16*tid+15
@@ -104,36 +128,24 @@ __global__ __launch_bounds__(kRNT, 1) void k_index_topk_ranges(IndexArgs a, int 
   uint32_t T = 0u, need = 0u;
   int pp = 0;
   if (nr > K) {
-    uint32_t kmn = 0xffffffffu, kmx = 0u;
-#pragma unroll
-    for (int j = 0; j < kRPer; ++j) {
-      if (key[j]) {
-        kmn = min(kmn, key[j]);
-        kmx = max(kmx, key[j]);
-      }
-    }
-    kmn = wave_all(kmn, 0xffffffffu, OpMin{});
-    kmx = wave_all(kmx, 0u, OpMax{});
-    if (lane == 0) {
-      sh.red[0][w] = kmn;
-      sh.red[1][w] = kmx;
-    }
-    __syncthreads();
-    kmn = waves_all<kRNW>(sh.red[0], 0xffffffffu, OpMin{});
-    kmx = waves_all<kRNW>(sh.red[1], 0u, OpMax{});
+    const uint32_t kmn = waves_all<kRNW>(sh.red[0], 0xffffffffu, OpMin{});
+    const uint32_t kmx = waves_all<kRNW>(sh.red[1], 0u, OpMax{});
     uint32_t lo = kmn;
     uint64_t range = kmx >= kmn ? (uint64_t)kmx - kmn + 1 : 1;
     need = (uint32_t)K;
-    bool ranked = false;
+    bool ranked = false, first = true;
     // Each pass narrows [lo, lo + range) to the bin holding the need-th
     // largest remaining key.  Once that bin holds at most kRList keys, they
     // are ranked directly under (key desc, position asc) instead.
     while (range > 1) {
       const int shift = bin_shift(range);
       const int nb = (int)((range - 1) >> shift) + 1;
-      for (int i = tid; i < kRBins; i += kRNT) sh.hist[i] = 0;
-      if (tid == 0) sh.list_n = 0;
-      __syncthreads();
+      if (!first) {  // the first pass's bins were cleared before the scores
+        for (int i = tid; i < kRBins; i += kRNT) sh.hist[i] = 0;
+        if (tid == 0) sh.list_n = 0;
+        __syncthreads();
+      }
+      first = false;
 #pragma unroll
       for (int j = 0; j < kRPer; ++j) {
         const uint32_t k = key[j];

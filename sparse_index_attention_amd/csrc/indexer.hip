@@ -66,7 +66,9 @@ __global__ __launch_bounds__(256) void k_index_scores_f32(IndexArgs a) {
 template <int HI, bool MX>
 __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_qblocks, int n_chunks,
                                                              int chunks_per_item) {
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform values are kept in scalar registers (readfirstlane), so that
+  // the page and row descriptors built from them are scalar too
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n_ranges = (n_chunks + chunks_per_item - 1) / chunks_per_item;
   const int64_t items = (int64_t)n_qblocks * n_ranges;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -75,8 +77,8 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
     const int rg = (int)(it % n_ranges);
     const int t = qb * 4 + wave;
     if (t >= a.s.T) continue;
-    const int pos = clampi(a.s.q_pos[t], -1, a.s.max_visible - 1);
-    const int b = clampi(a.s.q_seq[t], 0, a.s.batch - 1);
+    const int pos = __builtin_amdgcn_readfirstlane(clampi(a.s.q_pos[t], -1, a.s.max_visible - 1));
+    const int b = __builtin_amdgcn_readfirstlane(clampi(a.s.q_seq[t], 0, a.s.batch - 1));
     const int c_begin = rg * chunks_per_item;
     int c_end = c_begin + chunks_per_item;
     c_end = c_end < n_chunks ? c_end : n_chunks;
@@ -86,7 +88,14 @@ __global__ __launch_bounds__(256, 2) void k_index_scores_fp8(IndexArgs a, int n_
 
     float* srow = a.scores + (int64_t)t * a.ld;
     score_pages<HI, MX>(a, t, pos, b, c_begin, c_end, [&](int s, float score) __attribute__((always_inline)) {
-      if (s < a.s.max_visible) srow[s] = score;
+      // a descriptor over the row from this page on, ending at max_visible:
+      // its range check drops the stores past the row's end, with no branch
+      const int s0 = __builtin_amdgcn_readfirstlane(s) & ~63;   // 64c (lane 0 holds key 64c)
+      const uint64_t ra = (uint64_t)(uintptr_t)(srow + s0);
+      void* rp = (void*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ra >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ra));
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(rp, 0, (a.s.max_visible - s0) * 4, kRawBuffer);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), prs, (s - s0) * 4, 0, 0);
     });
   }
 }
@@ -353,6 +362,8 @@ hipError_t launch_index_scores(const sia_indexer_in& in, const SeqArgs& s, float
   const int cus = num_cus();
   const int64_t target_items = (int64_t)cus * 2;
   int n_ranges = (int)((target_items + n_qblocks - 1) / n_qblocks);
+  // at most 64 pages per item: a wave holds its item's page ids one per lane
+  n_ranges = max(n_ranges, (n_chunks + 63) / 64);
   n_ranges = n_ranges < 1 ? 1 : (n_ranges > n_chunks ? n_chunks : n_ranges);
   const int cpi = (n_chunks + n_ranges - 1) / n_ranges;
   const int64_t items = (int64_t)n_qblocks * ((n_chunks + cpi - 1) / cpi);
