@@ -44,7 +44,7 @@ constexpr int kMaxK = 2048;
 constexpr int kMaxBin = 256;
 constexpr int kBuf = kMaxK + kMaxBin;
 constexpr int kStreamWords = 8192;  // order-1 bitmap of streamed rows: 262144 positions
-constexpr int kDirect = 4096;
+constexpr int kDirect = 8192;  // rows up to this long histogram every key (no sample bound)
 constexpr int kStreamLoads = 8;     // loads in flight per thread in a streamed pass
 
 // ---- exact path ----------------------------------------------------------------
