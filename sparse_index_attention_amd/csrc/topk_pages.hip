@@ -39,18 +39,30 @@ __global__ __launch_bounds__(kPMThreads) void k_page_max(const float* __restrict
   if (c == 0 && threadIdx.x == 0) plast[t] = n > 0 ? (n - 1) >> 6 : -1;
   const int sub = threadIdx.x & 15;
   const float* row = scores + (int64_t)t * ld;
+  // The four rounds' loads are unconditional and issued together: this
+  // workgroup's part of the row goes through a buffer descriptor that ends at
+  // the first group of four past the row's visible entries (lim rounded up to
+  // 4 is still inside the row, ld being a multiple of 4), loads past it
+  // return zeros, and positions at or past n are masked to key 0 afterwards.
+  // A conditional load per round cost one memory latency each.
+  const int64_t x0 = (int64_t)c * kPMPages * kPage;  // first position of this workgroup's pages
+  int64_t span = ((lim + 3) & ~(int64_t)3) - x0;
+  span = span < 0 ? 0 : (span > kPMPages * kPage ? kPMPages * kPage : span);
+  const __amdgpu_buffer_rsrc_t rrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(row + x0), 0, (int)(span * 4), kRawBuffer);
+  v4i v[kPMPages / 16];
+#pragma unroll
+  for (int r = 0; r < kPMPages / 16; ++r) {
+    const int lp = r * 16 + (int)(threadIdx.x >> 4);   // page within the workgroup's 64
+    v[r] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rrs, (lp * kPage + sub * 4) * 4, 0, 0));
+  }
 #pragma unroll
   for (int r = 0; r < kPMPages / 16; ++r) {
     const int p = c * kPMPages + r * 16 + (int)(threadIdx.x >> 4);
     const int x = p * kPage + sub * 4;
     uint32_t k = 0u;  // below every float's key
-    if (x < n) {      // x + 3 < ld: ld and x are multiples of 4 and x < n <= ld
-      const float4 v = *reinterpret_cast<const float4*>(row + x);
-      k = f2key(v.x);
-      if (x + 1 < n) k = max(k, f2key(v.y));
-      if (x + 2 < n) k = max(k, f2key(v.z));
-      if (x + 3 < n) k = max(k, f2key(v.w));
-    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) k = max(k, f2key(__int_as_float(v[r][q])) & (uint32_t)((x + q - n) >> 31));
     k = row_incl(k, 0u, OpMax{});  // lane 15 of each 16-lane row: the page maximum
     if (sub == 15 && p * kPage < n) pscore[(int64_t)t * ldp + p] = key2f(k);
   }
