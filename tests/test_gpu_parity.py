@@ -11,8 +11,8 @@ import oracle as O
 from sparse_index_attention_amd import sia
 from sparse_index_attention_amd import workloads as W
 
-from gpu_support import (check_attention, check_scores, dev, kind_of, page_band_ok, page_max, tie_band_ok,
-                         to_np_out, upload, workload)
+from gpu_support import (ATT_TOL, LSE_ATOL, check_attention, check_scores, dev, kind_of, page_band_ok, page_max,
+                         tie_band_ok, to_np_out, upload, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -187,6 +187,42 @@ def test_sparse_mla_all_invalid_row_gives_zero_and_neg_inf():
         assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
         row0 = O.kv_rows(wl.oracle_kv(), O.physical_slots(wl.block_table[1], np.array([0]), 64))
         assert np.allclose(o[1], np.broadcast_to(row0[:, :512], (wl.cfg["H"], 512)), atol=1e-2, rtol=1e-2)
+
+
+@pytest.mark.parametrize("name", ["decode_tiny", "quant_decode_tiny", "prefill_tiny"])
+def test_dense_causal_attention_when_K_covers_the_context(name):
+    """Rows whose visible count is at most K select every visible position
+    (exactly, whatever the scores), so the fused call reduces to dense causal
+    MLA attention there.  The reference is a float64 softmax over all visible
+    rows, taken here with torch from the decoded cache rows, not through the
+    oracle's sparse attention."""
+    wl = workload(name)
+    K, H, Dc = wl.cfg["K"], wl.cfg["H"], wl.cfg["Dc"]
+    rows = [t for t in range(wl.Tq) if int(wl.q_pos[t]) + 1 <= K]
+    print(f"[dense] {name}: {len(rows)} rows with K >= context", flush=True)
+    assert rows, "the workload should have rows that K covers"
+    seq, ix, q, kv = upload(wl)
+    idx = torch.empty(wl.Tq, K, dtype=torch.int32, device="cuda")
+    lse = torch.empty(wl.Tq, H, dtype=torch.float32, device="cuda")
+    out = sia.index_select_attend(ix, q, kv, seq, K, wl.softmax_scale, order=1, idx_out=idx, lse=lse)
+    torch.cuda.synchronize()
+    ids, o, l = idx.cpu().numpy(), to_np_out(out), lse.cpu().numpy()
+    kvd = wl.oracle_kv()
+    qd = torch.from_numpy(O.decode_bf16(wl.q).astype(np.float64))
+    atol, rtol = ATT_TOL[kind_of(wl)]
+    for t in rows:
+        n = int(wl.q_pos[t]) + 1
+        # order 1: every visible position in ascending order, then -1
+        assert np.array_equal(ids[t][:n], np.arange(n)) and np.all(ids[t][n:] == -1), f"row {t}: selection"
+        b = int(wl.q_seq[t])
+        kr = torch.from_numpy(O.kv_rows(kvd, O.physical_slots(wl.block_table[b], np.arange(n), 64)).astype(np.float64))
+        logits = wl.softmax_scale * (qd[t] @ kr.T)                    # [H, n]
+        ref = torch.softmax(logits, dim=1) @ kr[:, :Dc]               # [H, Dc]
+        ref_lse = torch.logsumexp(logits, dim=1)
+        err = np.abs(o[t] - ref.numpy())
+        assert np.all(err <= atol + rtol * np.abs(ref.numpy())), f"row {t}: max err {err.max()}"
+        assert np.all(np.abs(l[t] - ref_lse.numpy()) <= LSE_ATOL[kind_of(wl)] + 1e-4 * np.abs(ref_lse.numpy())), \
+            f"row {t}: lse"
 
 
 @pytest.mark.parametrize("name", TINY)
