@@ -62,3 +62,40 @@ def test_noalloc_matches_workspace_call_twice():
 def test_noalloc_small_prefill_and_page_selection():
     compare("chunked_prefill_tiny", 1)
     compare("quant_decode_tiny", 2)
+
+
+def test_noalloc_replays_from_a_captured_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture.  The call is captured once and replayed three times, with eager
+    work (the outputs overwritten, an unrelated kernel) and synchronisations
+    between replays; every replay must give the eager call's bits."""
+    name, order = "decode_tiny", 0
+    print(f"[noalloc-graph] {name}: eager reference", flush=True)
+    wl = W.make_workload(name)
+    K, H, Dc = wl.cfg["K"], wl.cfg["H"], wl.cfg["Dc"]
+    seq, ix, q, kv = upload(wl)
+    idx = torch.empty((wl.Tq, K), dtype=torch.int32, device="cuda")
+    lse = torch.empty((wl.Tq, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.Tq, H, Dc), dtype=q.dtype, device="cuda")
+    # eager call first: it also looks up the array's address, outside the capture
+    assert noalloc_raw(ix, q, kv, seq, K, wl.softmax_scale, order, idx, out, lse) == 0
+    torch.cuda.synchronize()
+    ref = (idx.cpu().numpy(), out.view(torch.int16).cpu().numpy(), lse.view(torch.int32).cpu().numpy())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rc = noalloc_raw(ix, q, kv, seq, K, wl.softmax_scale, order, idx, out, lse)
+    assert rc == 0, sia.lib().sia_status_string(rc)
+    torch.cuda.synchronize()
+    junk = torch.ones(1 << 20, device="cuda")
+    for rep in range(3):
+        idx.fill_(-7)
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        junk.mul_(1.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (idx.cpu().numpy(), out.view(torch.int16).cpu().numpy(), lse.view(torch.int32).cpu().numpy())
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), f"replay {rep} differs from the eager call"
+        print(f"[noalloc-graph] replay {rep}: identical", flush=True)
