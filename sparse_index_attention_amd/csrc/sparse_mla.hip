@@ -187,7 +187,12 @@ constexpr int kVT = kVH / 32;  // 32-column output tiles per half
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
 template <int N> __device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N)); }
 
-template <int NW, bool FP8, bool BUF>
+// RS (fp8 only): the latent part of a row has one scale (tiles of 512
+// elements).  The codes are then staged exactly (e4m3 -> bf16 is exact), and
+// the scale moves onto the row's latent score (s * S_latent + S_rope) and onto
+// its softmax weight in P before the P.V product, instead of scaling each of
+// the 512 elements while staging.
+template <int NW, bool FP8, bool BUF, bool RS = false>
 __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   constexpr int NT = NW * 64;
   constexpr int HBW = NW / 2;                  // head blocks per workgroup
@@ -206,6 +211,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t sslot[RMAX * NT];
   __shared__ __attribute__((aligned(16))) float smask[RMAX * NT];  // 0 or -inf per row
   __shared__ __attribute__((aligned(16))) float4 xbuf[2 * NW * 4 * 64];   // partial S^T exchange, two parities
+  // RS: latent scale of each row of the three tile buffers (0 for a row without an index)
+  __shared__ __attribute__((aligned(16))) float tscl[RS ? 3 * kRowsTile : 4];
 
   // block -> (token, split, head part).  Workgroups are dispatched to the
   // eight XCDs round-robin (block b on XCD b % 8), so every workgroup of token
@@ -308,10 +315,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       for (int m = 0; m < kFp8Loads; ++m) {
         const int c = f_sub + TPR * m;
         stage[m] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(kv8rs, row_off, 16 * TPR * m, 0));
-        // latent chunks take their tile's scale, the rope chunks 1 (0 for a row without an index)
-        const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, sc_off + 4u * ((16u * c) >> le), 0, 0));
-        stage_scale[m] = c < 32 ? sc : (valid ? 1.f : 0.f);
+        if constexpr (!RS) {
+          // latent chunks take their tile's scale, the rope chunks 1 (0 for a row without an index)
+          const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, sc_off + 4u * ((16u * c) >> le), 0, 0));
+          stage_scale[m] = c < 32 ? sc : (valid ? 1.f : 0.f);
+        }
       }
+      // RS: the row's one latent scale (0 past the range)
+      if constexpr (RS) stage_scale[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, sc_off, 0, 0));
     } else {
       const unsigned char* src = kvb + (int64_t)slot * 640 + 16 * f_sub;
 #pragma unroll
@@ -319,26 +330,41 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
         const int c = f_sub + TPR * m;
         const v4i v = *(const v4i*)(src + 16 * TPR * m);
         stage[m] = valid ? v : v4i{0, 0, 0, 0};
-        const float sc = c < 32 ? a.kv_scale[sbase + ((16 * c) >> le)] : 1.f;
-        stage_scale[m] = valid ? sc : 0.f;
+        if constexpr (!RS) {
+          const float sc = c < 32 ? a.kv_scale[sbase + ((16 * c) >> le)] : 1.f;
+          stage_scale[m] = valid ? sc : 0.f;
+        }
       }
+      if constexpr (RS) stage_scale[0] = valid ? a.kv_scale[sbase] : 0.f;
     }
   };
-  auto commit_fp8 = [&](lds_u8* dst) __attribute__((always_inline)) {
+  auto commit_fp8 = [&](lds_u8* dst, float* sdst) __attribute__((always_inline)) {
     const int r = f_row, sw = swz(r);
+    if constexpr (RS) {
+      if (f_sub == 0) sdst[r] = stage_scale[0];
+    }
 #pragma unroll
     for (int m = 0; m < kFp8Loads; ++m) {
       const int c = f_sub + TPR * m;
       const v4i v = stage[m];
       if (c < 32) {
-        const float sc = stage_scale[m];
         uint32_t o[8];
+        if constexpr (RS) {
+          // exact conversion, two codes per instruction (scale operand 1)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float2 f0 = fp8x2_to_f32<false>((uint32_t)v[w]);
-          const float2 f1 = fp8x2_to_f32<true>((uint32_t)v[w]);
-          o[2 * w] = pack_bf16x2(f0.x * sc, f0.y * sc);
-          o[2 * w + 1] = pack_bf16x2(f1.x * sc, f1.y * sc);
+          for (int w = 0; w < 4; ++w) {
+            o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[w], 1.f, false));
+            o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[w], 1.f, true));
+          }
+        } else {
+          const float sc = stage_scale[m];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float2 f0 = fp8x2_to_f32<false>((uint32_t)v[w]);
+            const float2 f1 = fp8x2_to_f32<true>((uint32_t)v[w]);
+            o[2 * w] = pack_bf16x2(f0.x * sc, f0.y * sc);
+            o[2 * w + 1] = pack_bf16x2(f1.x * sc, f1.y * sc);
+          }
         }
         const int c0 = 2 * c, c1 = 2 * c + 1;
         *(lds_v4i*)(dst + ((c0 >> 3) * 256 + r * 8 + ((c0 & 7) ^ sw)) * 16) =
@@ -425,6 +451,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   lds_u8* const T0 = (lds_u8*)tile0;
   lds_u8* const T1 = (lds_u8*)tile1;
   lds_u8* const T2 = (lds_u8*)tile2;
+  // RS: the row-scale array of a tile buffer (resolved at compile time: the
+  // buffers are passed as the constants above)
+  auto scl_of = [&](lds_u8* b) __attribute__((always_inline)) -> float* {
+    if constexpr (RS) return tscl + kRowsTile * (b == T0 ? 0 : (b == T1 ? 1 : 2));
+    return tscl;
+  };
   __syncthreads();
   {
   // ---- software-pipelined tiles ------------------------------------
@@ -456,8 +488,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   constexpr int PF = 6, PFV = 6;
   // partial S^T of the tile in `buf` over this wave's half of the depth;
   // between(j) runs after the MFMA of step j
-  auto s_partial = [&](lds_u8* buf, auto&& between) __attribute__((always_inline)) -> v16f {
+  // RS: the wave's last two steps are rope depth (global steps 32 + 2ch and
+  // 33 + 2ch); they accumulate apart, and the partial is s * latent + rope
+  // with the scales `scl` of the tile's rows
+  auto s_partial = [&](lds_u8* buf, const float* scl, auto&& between) __attribute__((always_inline)) -> v16f {
     v16f acc = v16f{};
+    v16f accr = v16f{};
     v8bf kring[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) kring[j] = *(lds_v8bf*)(buf + sbase[j & 1] + 4096 * (j >> 1));
@@ -465,8 +501,21 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     for (int j = 0; j < kHalfSteps; ++j) {
       const v8bf kf = kring[j % PF];
       if (j + PF < kHalfSteps) kring[j % PF] = *(lds_v8bf*)(buf + sbase[(j + PF) & 1] + 4096 * ((j + PF) >> 1));
-      acc = mfma_bf16(kf, qb[j], acc);
+      if (RS && j >= kHalfSteps - 2)
+        accr = mfma_bf16(kf, qb[j], accr);
+      else
+        acc = mfma_bf16(kf, qb[j], acc);
       between(j);
+    }
+    if constexpr (RS) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 s4 = *(const float4*)(scl + 8 * k + 4 * hh);
+        acc[4 * k] = fmaf(s4.x, acc[4 * k], accr[4 * k]);
+        acc[4 * k + 1] = fmaf(s4.y, acc[4 * k + 1], accr[4 * k + 1]);
+        acc[4 * k + 2] = fmaf(s4.z, acc[4 * k + 2], accr[4 * k + 2]);
+        acc[4 * k + 3] = fmaf(s4.w, acc[4 * k + 3], accr[4 * k + 3]);
+      }
     }
     return acc;
   };
@@ -512,6 +561,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       for (int k = 0; k < kRG; ++k) dsrc[k] = dma_src(i + 2, k);
     }
     const Flags fl = load_flags(i);
+    // RS: the latent scales of tile i's rows go onto their weights in P
+    Flags rsc{};
+    if constexpr (RS) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rsc.f[k] = *(const float4*)(scl_of(cur) + 8 * k + 4 * hh);
+    }
     // softmax of tile i (log2 domain; lane owns head nn, rows 8(r/4) + 4hh + r%4).
     // The maximum over both lane halves (one v_permlane32_swap) is needed only
     // until m_ref is set; afterwards each lane tracks its own maximum, for the
@@ -554,11 +609,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
           const int r = 2 * (j - 4) + rr;
           const float pv = fast_exp2(fmaf(sv[r], a.scale_log2, mneg));
           psum += pv;
-          pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
+          if constexpr (RS) {
+            const float4 f = rsc.f[r >> 2];
+            const float rs = (r & 3) == 0 ? f.x : (r & 3) == 1 ? f.y : (r & 3) == 2 ? f.z : f.w;
+            pb[r >> 3][r & 7] = static_cast<__bf16>(pv * rs);
+          } else {
+            pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
+          }
         }
       }
     };
-    v16f snext = s_partial(nxt, soft);
+    v16f snext = s_partial(nxt, scl_of(nxt), soft);
     // O^T += V^T . P^T for tile i; MFMA mf covers tile rows 16mf + R(hh, jj)
     auto vfrag = [&](int vt, int mf) -> v8bf {
       const int imm = 4096 * (vt >> 1) + 2048 * mf;
@@ -579,7 +640,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     // the partial scores of tile i+1 go out after the output MFMAs are issued:
     // by then the score chain has finished, so the writes do not wait for it
     xwrite(snext, (i + 1) & 1);
-    if constexpr (FP8) commit_fp8(fut);  // tile i+2: buffer free since the last barrier
+    if constexpr (FP8) commit_fp8(fut, scl_of(fut));  // tile i+2: buffer free since the last barrier
     l_run += psum;
     // tile i+2 is in LDS and the partial scores of tile i+1 are published
     wait_vm_lgkm0<0>();
@@ -598,9 +659,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     // prologue: tiles 0 and 1 in LDS, full scores of tile 0
     if constexpr (FP8) {
       issue_fp8(0);
-      commit_fp8(T0);
+      commit_fp8(T0, scl_of(T0));
       issue_fp8(1);
-      commit_fp8(T1);
+      commit_fp8(T1, scl_of(T1));
     } else {
       issue_dma(0, T0);
       issue_dma(1, T1);
@@ -608,7 +669,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     wait_vm_lgkm0<0>();
     asm volatile("s_barrier" ::: "memory");
     // this wave's half of the scores of tile 0; iteration 0 adds the partner's
-    sacc = s_partial(T0, [](int) {});
+    sacc = s_partial(T0, scl_of(T0), [](int) {});
     xwrite(sacc, 0);
     wait_vm_lgkm0<63>();
     asm volatile("s_barrier" ::: "memory");
@@ -792,11 +853,17 @@ hipError_t launch_sparse_mla(const void* q, int heads, const sia_kv_in& kv, cons
   // fp8 rows are 640 bytes; the scale array must fit a descriptor too
   const uint64_t sc_entries = ((uint64_t)s.num_pages * kPage * kDc) >> (a.log2_scale_tokens + a.log2_scale_elems);
   const bool buf8 = (uint64_t)s.num_pages * kPage * 640 <= 0xfffff000ull && sc_entries * 4 <= 0xfffff000ull;
-#define SIA_LAUNCH_MLA(NW)                                                                   \
-  if (fp8 && buf8)                                                                           \
-    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, true>), grid, dim3(NW * 64), 0, st, a);  \
-  else if (fp8)                                                                              \
-    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, false>), grid, dim3(NW * 64), 0, st, a); \
+  // one latent scale per row (tiles of 512 elements): the scale goes onto scores and P
+  const bool rs = kv.scale_elems == kDc;
+#define SIA_LAUNCH_MLA(NW)                                                                         \
+  if (fp8 && buf8 && rs)                                                                           \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, true, true>), grid, dim3(NW * 64), 0, st, a);  \
+  else if (fp8 && buf8)                                                                            \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, true>), grid, dim3(NW * 64), 0, st, a);        \
+  else if (fp8 && rs)                                                                              \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, false, true>), grid, dim3(NW * 64), 0, st, a); \
+  else if (fp8)                                                                                    \
+    hipLaunchKernelGGL((k_sparse_mla_mfma<NW, true, false>), grid, dim3(NW * 64), 0, st, a);       \
   else if (buf)                                                                              \
     hipLaunchKernelGGL((k_sparse_mla_mfma<NW, false, true>), grid, dim3(NW * 64), 0, st, a); \
   else                                                                                       \
