@@ -261,10 +261,12 @@ __device__ __forceinline__ void for_keys(const uint32_t (&key)[PER > 0 ? PER : 1
 // the row from memory on every pass.  CAND: the rows are candidate lists with a
 // map back to positions; with PER <= 32 each thread also holds the positions
 // of its keys, so that score-order output needs no dependent load of the map.
+// Rows of n keys with n_lo < n <= n_hi are this launch's; the others belong to
+// another launch (another PER) and their workgroups return at once.
 template <int PER, bool CAND>
 __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, int64_t ld, SeqArgs s, int K,
                                               int order, int32_t* __restrict__ idx, float* __restrict__ vals,
-                                              CandMap cm) {
+                                              CandMap cm, int n_lo, int n_hi) {
   constexpr bool kCarry = CAND && PER > 0 && PER <= 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   TopkSmem<PER>& smem = *reinterpret_cast<TopkSmem<PER>*>(smem_raw);
@@ -286,6 +288,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
     const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
     n = clampi(s.q_pos[t], -1, (int)lim - 1) + 1;
   }
+  if (n <= n_lo || n > n_hi) return;
   const float* row = scores + (int64_t)t * ld;
   int32_t* orow = idx + (int64_t)t * K;
   float* vrow = vals ? vals + (int64_t)t * K : nullptr;
@@ -506,30 +509,47 @@ __global__ __launch_bounds__(kNT) void k_topk(const float* __restrict__ scores, 
 
 template <int PER, bool CAND>
 static hipError_t launch_rows_as(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
-                                 float* vals, const CandMap& cm, hipStream_t st) {
+                                 float* vals, const CandMap& cm, int n_lo, int n_hi, hipStream_t st) {
   const size_t shm = sizeof(TopkSmem<PER>);
   hipError_t e =
       hipFuncSetAttribute((const void*)k_topk<PER, CAND>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_topk<PER, CAND>), dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals, cm);
+  hipLaunchKernelGGL((k_topk<PER, CAND>), dim3(s.T), dim3(kNT), shm, st, scores, ld, s, K, order, idx, vals, cm, n_lo,
+                     n_hi);
   return hipGetLastError();
 }
 template <int PER>
 static hipError_t launch_rows(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
-                              float* vals, const CandMap& cm, hipStream_t st) {
-  return cm.pos ? launch_rows_as<PER, true>(scores, ld, s, K, order, idx, vals, cm, st)
-                : launch_rows_as<PER, false>(scores, ld, s, K, order, idx, vals, cm, st);
+                              float* vals, const CandMap& cm, hipStream_t st, int n_lo = -1,
+                              int n_hi = 0x7fffffff) {
+  return cm.pos ? launch_rows_as<PER, true>(scores, ld, s, K, order, idx, vals, cm, n_lo, n_hi, st)
+                : launch_rows_as<PER, false>(scores, ld, s, K, order, idx, vals, cm, n_lo, n_hi, st);
 }
+
+// The rows of one call can differ in length (causal prefill: 1 .. max_visible
+// keys).  With many rows, each row goes to the smallest variant that holds
+// it, one launch per length class (the other classes' workgroups return at
+// once): variants with fewer keys per thread use fewer registers and run more
+// workgroups per CU, and rows that fit in registers are not streamed.  Few
+// rows (decode) keep one launch.
+constexpr int kClassMinRows = 1024;
 
 hipError_t launch_topk(const float* scores, int64_t ld, const SeqArgs& s, int K, int order, int32_t* idx,
                        float* vals, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int64_t lim = ld < (int64_t)s.max_visible ? ld : (int64_t)s.max_visible;
   const CandMap none{nullptr, 0, 0};
-  if (lim <= kNT * 8) return launch_rows<8>(scores, ld, s, K, order, idx, vals, none, st);
-  if (lim <= kNT * 32) return launch_rows<32>(scores, ld, s, K, order, idx, vals, none, st);
-  if (lim <= kNT * 64) return launch_rows<64>(scores, ld, s, K, order, idx, vals, none, st);
-  return launch_rows<0>(scores, ld, s, K, order, idx, vals, none, st);
+  const bool split = s.T >= kClassMinRows;
+  constexpr int c8 = kNT * 8, c32 = kNT * 32, c64 = kNT * 64;
+  hipError_t e;
+  if (lim <= c8) return launch_rows<8>(scores, ld, s, K, order, idx, vals, none, st);
+  if (split && (e = launch_rows<8>(scores, ld, s, K, order, idx, vals, none, st, -1, c8)) != hipSuccess) return e;
+  const int lo32 = split ? c8 : -1, lo64 = split ? c32 : -1, lo0 = split ? c64 : -1;
+  if (lim <= c32) return launch_rows<32>(scores, ld, s, K, order, idx, vals, none, st, lo32);
+  if (split && (e = launch_rows<32>(scores, ld, s, K, order, idx, vals, none, st, c8, c32)) != hipSuccess) return e;
+  if (lim <= c64) return launch_rows<64>(scores, ld, s, K, order, idx, vals, none, st, lo64);
+  if (split && (e = launch_rows<64>(scores, ld, s, K, order, idx, vals, none, st, c32, c64)) != hipSuccess) return e;
+  return launch_rows<0>(scores, ld, s, K, order, idx, vals, none, st, lo0);
 }
 
 hipError_t launch_topk_candidates(const float* cscore, const int32_t* cpos, int64_t ldc, int range_keys,

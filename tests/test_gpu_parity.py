@@ -129,6 +129,43 @@ def test_topk_edge_cases_cached_rows(K, order):
 
 
 @pytest.mark.parametrize("order", [0, 1])
+def test_topk_many_rows_of_every_length_class(order):
+    """Calls with many rows send each row to the variant that holds its length
+    (keys per thread 8, 32, 64, or streamed), one launch per class.  Every row
+    must be handled by exactly one launch: no row keeps the sentinel the output
+    was filled with, each is a valid selection (distinct visible positions,
+    -1 padding), and two rows of every length equal the oracle bit for bit."""
+    K = 2048
+    lens = [0, 1, 100, 2048, 8192, 8193, 20000, 32768, 32769, 50000, 65536, 65537, 70001]
+    T = 1200
+    print(f"[topk-classes] order={order}: {T} rows", flush=True)
+    n = np.array([lens[t % len(lens)] for t in range(T)], np.int64)
+    mv = int(n.max())
+    ld = (mv + 3) // 4 * 4
+    rng = np.random.default_rng(77 + order)
+    scores = torch.from_numpy(rng.standard_normal((T, ld), dtype=np.float32)).cuda()
+    pages = (mv + 63) // 64
+    seq = sia.SeqMap(dev(np.zeros(T, np.int32)), dev((n - 1).astype(np.int32)),
+                     dev(np.arange(pages, dtype=np.int32)[None]), pages, mv)
+    idx = torch.full((T, K), -7, dtype=torch.int32, device="cuda")
+    sia.topk(scores, seq, K, order=order, idx=idx)
+    torch.cuda.synchronize()
+    ids = idx.cpu().numpy()
+    for t in range(T):
+        m = min(int(n[t]), K)
+        row = ids[t]
+        assert np.all(row[m:] == -1), f"row {t} (n={n[t]}): padding"
+        sel = row[:m]
+        assert np.all((sel >= 0) & (sel < n[t])) and len(np.unique(sel)) == m, f"row {t} (n={n[t]}): selection"
+    sc = None
+    for t in range(2 * len(lens)):
+        if sc is None or t % 4 == 0:
+            sc = scores[t: t + 4].cpu().numpy()
+        exp = O.topk_row(sc[t % 4][: int(n[t])], K, order)
+        assert np.array_equal(ids[t], exp), f"row {t} (n={n[t]})"
+
+
+@pytest.mark.parametrize("order", [0, 1])
 def test_topk_long_rows_uncached(order):
     print(f"[topk-long] order={order}", flush=True)
     ns = [70000, 40000, 1, 2048, 65536, 100003]
