@@ -108,14 +108,16 @@ def write_traffic(workload, fetch_csv, write_csv):
         factor = COPY_PROBE_BYTES / (1024.0 * sorted(copies)[len(copies) // 2])
         out[f"{label}_factor"] = factor
         for k, (subs, _) in TRAFFIC_KERNELS.items():
-            # one launch of `k` = one dispatch of each of its kernels that ran
-            # (the split merge runs only when rows are split): pair them up in order
+            # one launch of `k` = one call of its entry point.  The first of its
+            # kernels that ran runs once per call; the others add every dispatch
+            # they make (the split merge runs only when rows are split, and the
+            # Top-K launches once per row-length class of a call with many rows)
             per = [sorted((d for d in vals if s in names[d]), key=int) for s in subs]
             per = [x for x in per if x]
             if not per:
                 continue
-            n = min(len(x) for x in per)
-            kib = sum(vals[x[i]] for x in per for i in range(n)) / n
+            n = len(per[0])
+            kib = sum(vals[d] for x in per for d in x) / n
             out["kernels"].setdefault(k, {})[f"{label}_bytes"] = kib * 1024.0 * factor
             out["kernels"][k]["launches"] = n
     for k, v in out["kernels"].items():
