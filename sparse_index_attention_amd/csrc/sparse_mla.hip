@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   int j1 = j0 + a.rows_per_split;
   j1 = j1 < a.K ? j1 : a.K;
   const int nrows = j1 > j0 ? j1 - j0 : 0;
-  const int ntiles = (nrows + kRowsTile - 1) / kRowsTile;
+  const int ntiles_split = (nrows + kRowsTile - 1) / kRowsTile;
   const int b = clampi(a.s.q_seq[t], 0, a.s.batch - 1);
   const int32_t* table = a.s.block_table + (int64_t)b * a.s.max_pages;
   const int32_t* irow = a.idx + (int64_t)t * a.K;
@@ -383,8 +383,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   // out first, then the query loads, then the page-table loads: loads complete
   // in order, so the page-table loads wait only for the indices, and the
   // query's 72 KB arrive while the table is resolved.
+  // Tiles past the split's last valid row hold only padding (a causal row
+  // with fewer visible positions than K ends in -1s): they would contribute
+  // exactly nothing, so the loop stops at the last tile with a valid row.
+  __shared__ int s_last[NW];
+  int last_ok = -1;
   {
-    const int rows = (ntiles + 2) * kRowsTile;
+    const int rows = (ntiles_split + 2) * kRowsTile;
     // loads are unconditional (clamped indices) so that none waits for another
     int pos[RMAX];
 #pragma unroll
@@ -410,8 +415,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const int pg = clampi(page[u], 0, a.s.num_pages - 1);
       sslot[r] = ok ? pg * kPage + (p & (kPage - 1)) : -1;
       smask[r] = ok ? 0.f : -INFINITY;
+      last_ok = ok ? r : last_ok;
     }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last_ok = max(last_ok, __shfl_xor(last_ok, o, 64));
+  if (lane == 0) s_last[wave] = last_ok;
   // keep the query operand resident: without this the compiler re-loads it
   // from memory inside the tile loop to save registers
 #pragma unroll
@@ -458,6 +467,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
     return tscl;
   };
   __syncthreads();
+  int last = s_last[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
+  const int ntiles = (last + kRowsTile) / kRowsTile;   // tiles up to the one holding row `last`
   {
   // ---- software-pipelined tiles ------------------------------------
   // Iteration i requests tile i+2 into the buffer tile i-1 used, computes the
