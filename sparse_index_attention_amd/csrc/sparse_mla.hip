@@ -415,11 +415,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
       const int pg = clampi(page[u], 0, a.s.num_pages - 1);
       sslot[r] = ok ? pg * kPage + (p & (kPage - 1)) : -1;
       smask[r] = ok ? 0.f : -INFINITY;
-      last_ok = ok ? r : last_ok;
+      // the wave's last valid row of this round, from one ballot (scalar)
+      const uint64_t bm = __builtin_amdgcn_ballot_w64(ok);
+      if (bm) last_ok = NT * u + 64 * wave + 63 - __builtin_clzll(bm);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last_ok = max(last_ok, __shfl_xor(last_ok, o, 64));
   if (lane == 0) s_last[wave] = last_ok;
   // keep the query operand resident: without this the compiler re-loads it
   // from memory inside the tile loop to save registers
@@ -470,7 +470,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_sparse_mla_mfma(MlaArgs a) {
   int last = s_last[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
-  const int ntiles = (last + kRowsTile) / kRowsTile;   // tiles up to the one holding row `last`
+  // tiles up to the one holding row `last`, in a scalar register (the same in
+  // every lane), so that the tile loop keeps scalar control
+  const int ntiles = __builtin_amdgcn_readfirstlane((last + kRowsTile) / kRowsTile);
   {
   // ---- software-pipelined tiles ------------------------------------
   // Iteration i requests tile i+2 into the buffer tile i-1 used, computes the
